@@ -1,0 +1,256 @@
+"""Python binding of libwf: the chunk-wise causal attention round of Wave Forcing on MI355X.
+
+Argument marshalling only. Every step of the round runs in the HIP kernels of
+``libwf.so`` (built by ``python -m chunk_causal_dit_amd.build``); torch is used
+to hold device memory and to name the stream. There is no fallback: if the
+library is missing, importing the calls raises.
+
+Calls mirror include/wf.h:
+    KVCache(...)                 wf_kv_pool_bytes / wf_kv_cache_create
+      .append / .refresh / .evict / .set_table / .table
+    rope3d(x, ...)               wf_rope3d (in place)
+    chunk_causal_attn_fwd(...)   wf_chunk_causal_attn_fwd
+    chunk_causal_attn_fwd_i8qk(...), attn_i8qk_workspace_bytes(...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Sequence, Tuple
+
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+__all__ = [
+    "WFError", "lib", "library_path", "exported_symbols", "header_symbols",
+    "WF_F32", "WF_BF16", "KVCache", "kv_pool_bytes", "rope3d",
+    "chunk_causal_attn_fwd", "attn_i8qk_workspace_bytes", "chunk_causal_attn_fwd_i8qk",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+HEADER = os.path.join(_ROOT, "include", "wf.h")
+
+WF_F32, WF_BF16 = 0, 1
+WF_KV_ADOPT, WF_KV_ZERO_FILL = 0, 1
+_DTYPE = {torch.float32: WF_F32, torch.bfloat16: WF_BF16}
+
+
+class WFError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__(f"{where}: status {status} ({text})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("WF_LIBRARY", os.path.join(_HERE, "libwf.so"))
+
+
+_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_SIGNATURES = {
+    "wf_kv_pool_bytes": (_c_size, [_c_int] * 5),
+    "wf_kv_cache_create": (_c_int, [ctypes.POINTER(_vp), _vp, _vp] + [_c_int] * 6 + [_vp]),
+    "wf_kv_cache_destroy": (_c_int, [_vp]),
+    "wf_kv_append": (_c_int, [_vp, _vp, _vp, _vp, ctypes.POINTER(_c_int)]),
+    "wf_kv_refresh": (_c_int, [_vp, _c_int, _vp, _vp, _vp]),
+    "wf_kv_evict": (_c_int, [_vp, _c_int]),
+    "wf_kv_set_table": (_c_int, [_vp, ctypes.POINTER(_c_int), _c_int]),
+    "wf_kv_get_table": (_c_int, [_vp, ctypes.POINTER(_c_int), _c_int, ctypes.POINTER(_c_int)]),
+    "wf_rope3d": (_c_int, [_vp] + [_c_int] * 11 + [ctypes.c_float, _vp]),
+    "wf_chunk_causal_attn_fwd": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp]),
+    "wf_attn_i8qk_workspace_bytes": (_c_size, [_vp, _c_int]),
+    "wf_chunk_causal_attn_fwd_i8qk": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp]),
+    "wf_status_str": (ctypes.c_char_p, [_c_int]),
+    "wf_last_error": (ctypes.c_char_p, []),
+    "wf_version": (_c_int, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libwf.so (loaded on first use; raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m chunk_causal_dit_amd.build`")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> List[str]:
+    """Function names declared in include/wf.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wf_[a-z0-9_]+)\s*\(", text)))
+
+
+def exported_symbols() -> List[str]:
+    """wf_* function names exported by the built library (dynamic symbol table)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    return sorted({l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("wf_")})
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        L = lib()
+        raise WFError(status, where, f"{L.wf_status_str(status).decode()}; {L.wf_last_error().decode()}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> _vp:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _vp(t.data_ptr())
+
+
+def kv_pool_bytes(n_slots: int, chunk_tokens: int, n_heads: int, head_dim: int, dtype: torch.dtype) -> int:
+    return int(lib().wf_kv_pool_bytes(n_slots, chunk_tokens, n_heads, head_dim, _DTYPE[dtype]))
+
+
+class KVCache:
+    """Ring-buffer history cache over two device pools (owned by this object)."""
+
+    def __init__(self, n_slots: int, chunk_tokens: int, n_heads: int, head_dim: int,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", stream=None):
+        if dtype not in _DTYPE:
+            raise ValueError(f"unsupported dtype {dtype}")
+        nbytes = kv_pool_bytes(n_slots, chunk_tokens, n_heads, head_dim, dtype)
+        if nbytes == 0:  # the shape check recorded why
+            raise WFError(-2, "wf_kv_pool_bytes", lib().wf_last_error().decode())
+        self.n_slots, self.chunk_tokens, self.n_heads, self.head_dim = n_slots, chunk_tokens, n_heads, head_dim
+        self.dtype = dtype
+        self.s_pad = (chunk_tokens + 127) // 128 * 128
+        self.k_pool = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.v_pool = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = _vp()
+        _check(lib().wf_kv_cache_create(ctypes.byref(h), _dev(self.k_pool, "k_pool"), _dev(self.v_pool, "v_pool"),
+                                        n_slots, chunk_tokens, n_heads, head_dim, _DTYPE[dtype],
+                                        WF_KV_ZERO_FILL, _vp(_stream(stream))), "wf_kv_cache_create")
+        self._h = h
+
+    # views of the pools in their documented layouts (for inspection and tests)
+    def k_slots(self) -> torch.Tensor:
+        return self.k_pool.view(self.dtype).view(self.n_slots, self.n_heads, self.s_pad, self.head_dim)
+
+    def v_slots(self) -> torch.Tensor:
+        return self.v_pool.view(self.dtype).view(self.n_slots, self.n_heads, self.head_dim, self.s_pad)
+
+    @property
+    def handle(self) -> _vp:
+        if self._h is None:
+            raise ValueError("cache is closed")
+        return self._h
+
+    def _chunk(self, t: torch.Tensor, name: str) -> _vp:
+        if t.dtype != self.dtype or tuple(t.shape) != (self.chunk_tokens, self.n_heads, self.head_dim):
+            raise ValueError(f"{name} must be {self.dtype} [{self.chunk_tokens}][{self.n_heads}][{self.head_dim}],"
+                             f" got {t.dtype} {tuple(t.shape)}")
+        return _dev(t, name)
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, stream=None) -> int:
+        slot = ctypes.c_int(-1)
+        _check(lib().wf_kv_append(self.handle, self._chunk(k, "k"), self._chunk(v, "v"), _vp(_stream(stream)),
+                                  ctypes.byref(slot)), "wf_kv_append")
+        return slot.value
+
+    def refresh(self, logical_idx: int, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+        _check(lib().wf_kv_refresh(self.handle, logical_idx, self._chunk(k, "k"), self._chunk(v, "v"),
+                                   _vp(_stream(stream))), "wf_kv_refresh")
+
+    def evict(self, n_oldest: int) -> None:
+        _check(lib().wf_kv_evict(self.handle, n_oldest), "wf_kv_evict")
+
+    def set_table(self, slots: Sequence[int]) -> None:
+        arr = (ctypes.c_int * max(1, len(slots)))(*slots)
+        _check(lib().wf_kv_set_table(self.handle, arr, len(slots)), "wf_kv_set_table")
+
+    def table(self) -> List[int]:
+        arr = (ctypes.c_int * 64)()
+        n = ctypes.c_int(0)
+        _check(lib().wf_kv_get_table(self.handle, arr, 64, ctypes.byref(n)), "wf_kv_get_table")
+        return list(arr[: n.value])
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            _lib.wf_kv_cache_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def rope3d(x: torch.Tensor, first_global_chunk: int, frames_per_chunk: int, grid_h: int, grid_w: int,
+           split: Tuple[int, int, int] = (44, 42, 42), theta: float = 10000.0, stream=None) -> torch.Tensor:
+    """In-place 3D rotary embedding of x [n_tokens][H][D]; returns x."""
+    if x.dim() != 3 or x.dtype not in _DTYPE:
+        raise ValueError("x must be [tokens][heads][head_dim] float32 or bfloat16")
+    n, H, D = x.shape
+    _check(lib().wf_rope3d(_dev(x, "x"), n, H, D, _DTYPE[x.dtype], first_global_chunk, frames_per_chunk,
+                           grid_h, grid_w, split[0], split[1], split[2], float(theta), _vp(_stream(stream))),
+           "wf_rope3d")
+    return x
+
+
+def _attn_io(q, cache, n_inflight, out, lse, with_lse):
+    nq = n_inflight * cache.chunk_tokens
+    shape = (nq, cache.n_heads, cache.head_dim)
+    if q.dtype != cache.dtype or tuple(q.shape) != shape:
+        raise ValueError(f"q must be {cache.dtype} {shape}, got {q.dtype} {tuple(q.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.dtype != q.dtype or tuple(out.shape) != shape:
+        raise ValueError("out must match q")
+    if lse is None and with_lse:
+        lse = torch.empty((cache.n_heads, nq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (cache.n_heads, nq)):
+        raise ValueError(f"lse must be float32 [{cache.n_heads}][{nq}]")
+    return out, lse
+
+
+def chunk_causal_attn_fwd(q: torch.Tensor, cache: KVCache, n_inflight: int, scale: float,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          with_lse: bool = True, stream=None):
+    """Chunk-wise causal attention of the round. Returns (out, lse or None)."""
+    out, lse = _attn_io(q, cache, n_inflight, out, lse, with_lse)
+    _check(lib().wf_chunk_causal_attn_fwd(_dev(q, "q"), cache.handle, n_inflight, float(scale), _dev(out, "out"),
+                                          _dev(lse, "lse") if lse is not None else None, _vp(_stream(stream))),
+           "wf_chunk_causal_attn_fwd")
+    return out, lse
+
+
+def attn_i8qk_workspace_bytes(cache: KVCache, n_inflight: int) -> int:
+    return int(lib().wf_attn_i8qk_workspace_bytes(cache.handle, n_inflight))
+
+
+def chunk_causal_attn_fwd_i8qk(q: torch.Tensor, cache: KVCache, n_inflight: int, scale: float,
+                               workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                               lse: Optional[torch.Tensor] = None, with_lse: bool = True, stream=None):
+    """int8-QK variant. Returns (out, lse or None)."""
+    out, lse = _attn_io(q, cache, n_inflight, out, lse, with_lse)
+    if workspace is None:
+        workspace = torch.empty(max(1, attn_i8qk_workspace_bytes(cache, n_inflight)), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().wf_chunk_causal_attn_fwd_i8qk(_dev(q, "q"), cache.handle, n_inflight, float(scale),
+                                               _dev(workspace, "workspace"), _dev(out, "out"),
+                                               _dev(lse, "lse") if lse is not None else None,
+                                               _vp(_stream(stream))),
+           "wf_chunk_causal_attn_fwd_i8qk")
+    return out, lse

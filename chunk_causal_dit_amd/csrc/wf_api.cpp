@@ -1,0 +1,267 @@
+// Host side of the C ABI: argument validation, the history-cache table and
+// the launch glue. Every check runs before any device work, so an error
+// return leaves the stream and the cache untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "wf_internal.h"
+
+namespace wf {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+static int ok() { return WF_OK; }
+
+static int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(WF_E_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static int check_shape(int n_slots, int chunk_tokens, int n_heads, int head_dim, int dtype) {
+  if (dtype_size(dtype) == 0) return fail(WF_E_DTYPE, "unknown dtype %d", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(WF_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (n_slots < 1 || n_slots > WF_MAX_TABLE)
+    return fail(WF_E_SHAPE, "n_slots %d outside [1, %d]", n_slots, WF_MAX_TABLE);
+  if (chunk_tokens < 1 || chunk_tokens > (1 << 20))
+    return fail(WF_E_SHAPE, "chunk_tokens %d outside [1, 2^20]", chunk_tokens);
+  if (n_heads < 1 || n_heads > 1024) return fail(WF_E_SHAPE, "n_heads %d outside [1, 1024]", n_heads);
+  return ok();
+}
+
+}  // namespace wf
+
+using namespace wf;
+
+WF_EXPORT size_t wf_kv_pool_bytes(int n_slots, int chunk_tokens, int n_heads, int head_dim, int dtype) {
+  if (check_shape(n_slots, chunk_tokens, n_heads, head_dim, dtype) != WF_OK) return 0;
+  return (size_t)n_slots * n_heads * pad_tokens(chunk_tokens) * head_dim * dtype_size(dtype);
+}
+
+WF_EXPORT int wf_kv_cache_create(wf_kv_cache** out, void* k_pool, void* v_pool, int n_slots,
+                                 int chunk_tokens, int n_heads, int head_dim, int dtype, int flags,
+                                 void* stream) {
+  if (!out || !k_pool || !v_pool) return fail(WF_E_NULL, "wf_kv_cache_create: NULL argument");
+  int st = check_shape(n_slots, chunk_tokens, n_heads, head_dim, dtype);
+  if (st != WF_OK) return st;
+  if (!aligned(k_pool, 256) || !aligned(v_pool, 256))
+    return fail(WF_E_SHAPE, "wf_kv_cache_create: pools must be 256-byte aligned");
+  if (flags != WF_KV_ADOPT && flags != WF_KV_ZERO_FILL)
+    return fail(WF_E_SHAPE, "wf_kv_cache_create: unknown flags %d", flags);
+  auto* kv = new wf_kv_cache;
+  kv->k_pool = k_pool;
+  kv->v_pool = v_pool;
+  kv->n_slots = n_slots;
+  kv->chunk_tokens = chunk_tokens;
+  kv->n_heads = n_heads;
+  kv->head_dim = head_dim;
+  kv->dtype = dtype;
+  kv->s_pad = pad_tokens(chunk_tokens);
+  kv->esize = dtype_size(dtype);
+  kv->slot_elems = (size_t)n_heads * kv->s_pad * head_dim;
+  for (int s = 0; s < n_slots; ++s) kv->free_slots.push_back(s);
+  const size_t bytes = (size_t)n_slots * kv->slot_elems * kv->esize;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (flags == WF_KV_ZERO_FILL) {
+    e = launch_fill_zero(k_pool, bytes, s);
+    if (e == hipSuccess) e = launch_fill_zero(v_pool, bytes, s);
+  }
+  if (e != hipSuccess) {
+    delete kv;
+    return hip_status(e, "wf_kv_cache_create");
+  }
+  *out = kv;
+  return ok();
+}
+
+WF_EXPORT int wf_kv_cache_destroy(wf_kv_cache* kv) {
+  delete kv;
+  return WF_OK;
+}
+
+WF_EXPORT int wf_kv_append(wf_kv_cache* kv, const void* k, const void* v, void* stream, int* out_slot) {
+  if (!kv || !k || !v) return fail(WF_E_NULL, "wf_kv_append: NULL argument");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(WF_E_SHAPE, "wf_kv_append: k and v must be 16-byte aligned");
+  if (kv->free_slots.empty()) return fail(WF_E_FULL, "wf_kv_append: no free slot (%d slots)", kv->n_slots);
+  if ((int)kv->table.size() >= WF_MAX_TABLE)
+    return fail(WF_E_FULL, "wf_kv_append: table holds WF_MAX_TABLE entries");
+  const int slot = kv->free_slots.front();
+  hipError_t e = launch_kv_write(*kv, slot, k, v, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "wf_kv_append");
+  kv->free_slots.pop_front();
+  kv->table.push_back(slot);
+  if (out_slot) *out_slot = slot;
+  return ok();
+}
+
+WF_EXPORT int wf_kv_refresh(wf_kv_cache* kv, int logical_idx, const void* k, const void* v, void* stream) {
+  if (!kv || !k || !v) return fail(WF_E_NULL, "wf_kv_refresh: NULL argument");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(WF_E_SHAPE, "wf_kv_refresh: k and v must be 16-byte aligned");
+  if (logical_idx < 0 || logical_idx >= (int)kv->table.size())
+    return fail(WF_E_SLOT, "wf_kv_refresh: logical index %d outside table of %zu", logical_idx,
+                kv->table.size());
+  hipError_t e = launch_kv_write(*kv, kv->table[logical_idx], k, v, static_cast<hipStream_t>(stream));
+  return hip_status(e, "wf_kv_refresh");
+}
+
+WF_EXPORT int wf_kv_evict(wf_kv_cache* kv, int n_oldest) {
+  if (!kv) return fail(WF_E_NULL, "wf_kv_evict: NULL cache");
+  if (n_oldest < 0) return fail(WF_E_SHAPE, "wf_kv_evict: negative count %d", n_oldest);
+  if (n_oldest > (int)kv->table.size())
+    return fail(WF_E_EMPTY, "wf_kv_evict: %d entries requested, table holds %zu", n_oldest,
+                kv->table.size());
+  for (int i = 0; i < n_oldest; ++i) kv->free_slots.push_back(kv->table[i]);
+  kv->table.erase(kv->table.begin(), kv->table.begin() + n_oldest);
+  return ok();
+}
+
+WF_EXPORT int wf_kv_set_table(wf_kv_cache* kv, const int* slots, int n) {
+  if (!kv) return fail(WF_E_NULL, "wf_kv_set_table: NULL cache");
+  if (n < 0 || n > kv->n_slots) return fail(WF_E_SHAPE, "wf_kv_set_table: length %d outside [0, %d]", n, kv->n_slots);
+  if (n > 0 && !slots) return fail(WF_E_NULL, "wf_kv_set_table: NULL slots");
+  std::vector<char> used(kv->n_slots, 0);
+  for (int i = 0; i < n; ++i) {
+    if (slots[i] < 0 || slots[i] >= kv->n_slots)
+      return fail(WF_E_SLOT, "wf_kv_set_table: slot %d outside [0, %d)", slots[i], kv->n_slots);
+    if (used[slots[i]]) return fail(WF_E_SLOT, "wf_kv_set_table: slot %d listed twice", slots[i]);
+    used[slots[i]] = 1;
+  }
+  kv->table.assign(slots, slots + n);
+  kv->free_slots.clear();
+  for (int s = 0; s < kv->n_slots; ++s)
+    if (!used[s]) kv->free_slots.push_back(s);
+  return ok();
+}
+
+WF_EXPORT int wf_kv_get_table(const wf_kv_cache* kv, int* slots, int cap, int* n) {
+  if (!kv || !n) return fail(WF_E_NULL, "wf_kv_get_table: NULL argument");
+  if (cap < 0) return fail(WF_E_SHAPE, "wf_kv_get_table: negative capacity");
+  if (cap > 0 && !slots) return fail(WF_E_NULL, "wf_kv_get_table: NULL slots");
+  const int m = std::min<int>(cap, (int)kv->table.size());
+  for (int i = 0; i < m; ++i) slots[i] = kv->table[i];
+  *n = (int)kv->table.size();
+  return ok();
+}
+
+WF_EXPORT int wf_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dtype, int first_global_chunk,
+                        int frames_per_chunk, int grid_h, int grid_w, int d_t, int d_h, int d_w,
+                        float theta, void* stream) {
+  if (!x) return fail(WF_E_NULL, "wf_rope3d: NULL x");
+  if (!aligned(x, 16)) return fail(WF_E_SHAPE, "wf_rope3d: x must be 16-byte aligned");
+  if (dtype_size(dtype) == 0) return fail(WF_E_DTYPE, "wf_rope3d: unknown dtype %d", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(WF_E_UNSUPPORTED, "wf_rope3d: head_dim %d not supported", head_dim);
+  if (n_heads < 1 || frames_per_chunk < 1 || grid_h < 1 || grid_w < 1 || n_tokens < 0)
+    return fail(WF_E_SHAPE, "wf_rope3d: non-positive size");
+  if (d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 || d_t + d_h + d_w != head_dim)
+    return fail(WF_E_SHAPE, "wf_rope3d: split %d/%d/%d must be even and sum to %d", d_t, d_h, d_w, head_dim);
+  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(WF_E_SHAPE, "wf_rope3d: theta must be positive");
+  const long long chunk = (long long)frames_per_chunk * grid_h * grid_w;
+  if (chunk > (1 << 20) || n_tokens % chunk)
+    return fail(WF_E_SHAPE, "wf_rope3d: n_tokens %d is not a multiple of the chunk (%lld)", n_tokens, chunk);
+  if (first_global_chunk < 0) return fail(WF_E_SHAPE, "wf_rope3d: negative chunk index");
+  if ((double)frames_per_chunk * (first_global_chunk + n_tokens / chunk + 1) > 16777216.0)
+    return fail(WF_E_SHAPE, "wf_rope3d: frame positions exceed the exact fp32 integer range");
+  if (n_tokens == 0) return ok();
+  RopeTable t{};
+  const int seg[3] = {d_t, d_h, d_w};
+  int p = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int i = 0; i < seg[a] / 2; ++i, ++p) {
+      t.inv_freq[p] = (float)std::pow((double)theta, -2.0 * i / seg[a]);
+      t.axis[p] = a;
+    }
+  hipError_t e = launch_rope3d(x, n_tokens, n_heads, head_dim, dtype, first_global_chunk, frames_per_chunk,
+                               grid_h, grid_w, t, static_cast<hipStream_t>(stream));
+  return hip_status(e, "wf_rope3d");
+}
+
+static int fill_attn_params(const void* q, const wf_kv_cache* kv, int n_inflight, float scale, void* out,
+                            float* lse, AttnParams& p, const char* who) {
+  if (!q || !kv || !out) return fail(WF_E_NULL, "%s: NULL argument", who);
+  if (n_inflight < 1) return fail(WF_E_SHAPE, "%s: n_inflight %d < 1", who, n_inflight);
+  if ((int)kv->table.size() < n_inflight)
+    return fail(WF_E_EMPTY, "%s: n_inflight %d exceeds table length %zu", who, n_inflight, kv->table.size());
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(WF_E_SHAPE, "%s: scale must be positive and finite", who);
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(WF_E_SHAPE, "%s: q and out must be 16-byte aligned", who);
+  if (lse && !aligned(lse, 4)) return fail(WF_E_SHAPE, "%s: lse must be 4-byte aligned", who);
+  const long long nq = (long long)n_inflight * kv->chunk_tokens;
+  if (nq * kv->n_heads * kv->head_dim >= (1LL << 40)) return fail(WF_E_SHAPE, "%s: query block too large", who);
+  std::memset(&p, 0, sizeof p);
+  p.q = q;
+  p.o = out;
+  p.lse = lse;
+  p.k_pool = kv->k_pool;
+  p.v_pool = kv->v_pool;
+  p.slot_elems = (long long)kv->slot_elems;
+  p.n_heads = kv->n_heads;
+  p.chunk_tokens = kv->chunk_tokens;
+  p.s_pad = kv->s_pad;
+  p.n_inflight = n_inflight;
+  p.n_hist = (int)kv->table.size() - n_inflight;
+  p.scale_log2e = scale * 1.4426950408889634f;
+  for (size_t i = 0; i < kv->table.size(); ++i) p.slots[i] = kv->table[i];
+  return ok();
+}
+
+WF_EXPORT int wf_chunk_causal_attn_fwd(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
+                                       void* out, float* lse, void* stream) {
+  AttnParams p;
+  int st = fill_attn_params(q, kv, n_inflight, scale, out, lse, p, "wf_chunk_causal_attn_fwd");
+  if (st != WF_OK) return st;
+  return hip_status(launch_attn_fwd(*kv, p, static_cast<hipStream_t>(stream)), "wf_chunk_causal_attn_fwd");
+}
+
+WF_EXPORT size_t wf_attn_i8qk_workspace_bytes(const wf_kv_cache* kv, int n_inflight) {
+  if (!kv || n_inflight < 1 || n_inflight > (int)kv->table.size()) return 0;
+  if (kv->dtype != WF_BF16 || kv->head_dim != 128) return 0;
+  return i8_layout(*kv, n_inflight).total;
+}
+
+WF_EXPORT int wf_chunk_causal_attn_fwd_i8qk(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
+                                            void* workspace, void* out, float* lse, void* stream) {
+  const char* who = "wf_chunk_causal_attn_fwd_i8qk";
+  if (!workspace) return fail(WF_E_NULL, "%s: NULL workspace", who);
+  if (kv && kv->dtype != WF_BF16) return fail(WF_E_DTYPE, "%s: needs a bf16 cache", who);
+  if (kv && kv->head_dim != 128) return fail(WF_E_UNSUPPORTED, "%s: needs head_dim 128", who);
+  if (!aligned(workspace, 256)) return fail(WF_E_SHAPE, "%s: workspace must be 256-byte aligned", who);
+  AttnParams p;
+  int st = fill_attn_params(q, kv, n_inflight, scale, out, lse, p, who);
+  if (st != WF_OK) return st;
+  return hip_status(launch_attn_fwd_i8qk(*kv, p, workspace, scale, static_cast<hipStream_t>(stream)), who);
+}
+
+WF_EXPORT const char* wf_status_str(int status) {
+  switch (status) {
+    case WF_OK: return "WF_OK";
+    case WF_E_NULL: return "WF_E_NULL: NULL pointer argument";
+    case WF_E_SHAPE: return "WF_E_SHAPE: size out of range or inconsistent";
+    case WF_E_DTYPE: return "WF_E_DTYPE: unsupported element type";
+    case WF_E_SLOT: return "WF_E_SLOT: bad slot or logical index";
+    case WF_E_FULL: return "WF_E_FULL: no free slot";
+    case WF_E_EMPTY: return "WF_E_EMPTY: too few table entries";
+    case WF_E_UNSUPPORTED: return "WF_E_UNSUPPORTED: unsupported configuration";
+    case WF_E_HIP: return "WF_E_HIP: HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+WF_EXPORT const char* wf_last_error(void) { return g_last_error.c_str(); }
+
+WF_EXPORT int wf_version(void) { return 100; }  // 0.1.0

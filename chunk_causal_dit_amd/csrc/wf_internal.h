@@ -1,0 +1,86 @@
+// Internal declarations shared by the host glue (wf_api.cpp) and the kernel
+// translation units (*.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <deque>
+#include <vector>
+
+#include "wf.h"
+
+#define WF_EXPORT extern "C" __attribute__((visibility("default")))
+
+struct wf_kv_cache {
+  void* k_pool = nullptr;
+  void* v_pool = nullptr;
+  int n_slots = 0;
+  int chunk_tokens = 0;
+  int n_heads = 0;
+  int head_dim = 0;
+  int dtype = 0;
+  int s_pad = 0;            // chunk_tokens rounded up to a multiple of 128
+  size_t esize = 0;         // bytes per element
+  size_t slot_elems = 0;    // n_heads * s_pad * head_dim elements per slot (each pool)
+  std::vector<int> table;   // logical order, oldest first: physical slot ids
+  std::deque<int> free_slots;
+};
+
+namespace wf {
+
+constexpr int kSlotPadTokens = 128;
+
+inline int pad_tokens(int c) { return (c + kSlotPadTokens - 1) / kSlotPadTokens * kSlotPadTokens; }
+inline size_t dtype_size(int dtype) { return dtype == WF_F32 ? 4 : dtype == WF_BF16 ? 2 : 0; }
+
+// Records the message in the thread-local error slot and returns code.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// ---- kernel launchers (defined in the .hip files); each returns the launch status ----
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+hipError_t launch_kv_write(const wf_kv_cache& kv, int slot, const void* k, const void* v,
+                           hipStream_t s);
+
+struct RopeTable {
+  float inv_freq[64];
+  int axis[64];
+};
+hipError_t launch_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dtype,
+                         int first_global_chunk, int frames_per_chunk, int grid_h, int grid_w,
+                         const RopeTable& table, hipStream_t s);
+
+// Arguments of the attention kernels, passed by value (the slot table of the
+// visible chunks travels inside the launch, so later host edits never race).
+struct AttnParams {
+  const void* q;
+  void* o;
+  float* lse;
+  const void* k_pool;
+  const void* v_pool;
+  long long slot_elems;
+  int n_heads;
+  int chunk_tokens;
+  int s_pad;
+  int n_inflight;
+  int n_hist;
+  int q_tiles;     // query tiles per chunk
+  int key_tiles;   // key tiles per chunk
+  float scale_log2e;
+  int slots[WF_MAX_TABLE];  // physical slot of logical chunk c = 0..n_hist+n_inflight-1
+};
+
+hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& prm, hipStream_t s);
+
+// ---- int8-QK path ----
+struct I8Layout {
+  size_t q_codes, q_scales, k_codes, k_scales, mean, qm, partial, total;
+  int blocks_per_chunk;
+};
+I8Layout i8_layout(const wf_kv_cache& kv, int n_inflight);
+hipError_t launch_attn_fwd_i8qk(const wf_kv_cache& kv, AttnParams& prm, void* workspace,
+                                float scale, hipStream_t s);
+
+}  // namespace wf

@@ -1,0 +1,188 @@
+/*
+ * wf.h -- C ABI of libwf, the MI355X (gfx950) hot path of one Wave Forcing
+ * round: chunk-wise causal attention over a ring-buffer history cache.
+ *
+ * What a round is. Wave Forcing denoises several video chunks at staggered
+ * noise levels at once and re-runs a finished chunk to refresh the history
+ * cache, one output chunk per round (Wave Forcing paper pages, Abstract:
+ * "1F1C: one output chunk per concurrent forward round"). The in-flight
+ * chunks of a round (refresh chunk first, then the denoising chunks from
+ * cleanest to noisiest; README usage on the airadar.tv summaries: wp-size =
+ * step count + 1) form one query block. A chunk attends to the cached
+ * history, to every earlier (cleaner) in-flight chunk and to itself, never to
+ * a later one (Abstract: "chunk-wise causal attention to access earlier,
+ * cleaner chunks before their denoising is complete").
+ *
+ * Conventions shared by every call
+ *  - Pointers named k, v, q, x, out, workspace, lse, k_pool, v_pool are DEVICE
+ *    pointers; slots / out_slot / n are HOST pointers. The caller owns all
+ *    device memory. The library allocates only the small host cache handle;
+ *    no call allocates or frees device memory or synchronizes the device.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream). Every
+ *    device-side effect is enqueued on it; ordering is the stream's.
+ *  - Element types: WF_F32 (float) or WF_BF16 (bfloat16 stored as uint16).
+ *    Token-major layout [tokens][n_heads][head_dim], contiguous.
+ *  - Return value: WF_OK (0) or a negative WF_E_* code. On error nothing was
+ *    enqueued and the cache table is unchanged; wf_last_error() describes the
+ *    failure (thread-local). Device faults are asynchronous and surface at the
+ *    caller's next synchronization.
+ *  - A cache handle is not thread-safe.
+ */
+#ifndef WF_H
+#define WF_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define WF_OK 0
+#define WF_E_NULL (-1)        /* a required pointer is NULL                       */
+#define WF_E_SHAPE (-2)       /* a size is out of range or inconsistent           */
+#define WF_E_DTYPE (-3)       /* unknown element type, or not valid for the call  */
+#define WF_E_SLOT (-4)        /* slot / logical index out of range or duplicated  */
+#define WF_E_FULL (-5)        /* no free slot, or the table is at WF_MAX_TABLE    */
+#define WF_E_EMPTY (-6)       /* fewer table entries than the call needs          */
+#define WF_E_UNSUPPORTED (-7) /* head_dim not 64/128, or another unsupported mode */
+#define WF_E_HIP (-8)         /* a kernel launch was rejected by the HIP runtime  */
+
+/* ---- element types ---- */
+#define WF_F32 0
+#define WF_BF16 1
+
+/* Largest number of table entries (history + in-flight chunks) and slots. */
+#define WF_MAX_TABLE 64
+
+/* wf_kv_cache_create flags */
+#define WF_KV_ADOPT 0     /* take the pools as they are (padding already zero) */
+#define WF_KV_ZERO_FILL 1 /* enqueue a zero fill of both pools on the stream   */
+
+typedef struct wf_kv_cache wf_kv_cache;
+
+/* ------------------------------------------------------------------------
+ * History cache (Abstract: a history cache that later chunks read, and a
+ * cache-refresh stage that rewrites a finished chunk's K/V).
+ *
+ * Storage: two caller-owned device pools of n_slots chunk slots each.
+ * A slot holds one chunk of chunk_tokens tokens for all heads, padded to
+ * S_pad = chunk_tokens rounded up to a multiple of 128 tokens:
+ *   K pool: [n_slots][n_heads][S_pad][head_dim]   (token rows)
+ *   V pool: [n_slots][n_heads][head_dim][S_pad]   (transposed: key-contiguous)
+ * Padding is zero and stays zero. A host-side table lists the slots of the
+ * cache's chunks in logical order, oldest first; at attention time the last
+ * n_inflight entries are the in-flight chunks (refresh chunk first) and the
+ * entries before them are the history.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of ONE pool (K or V) for the given shape, padding included; 0 if the
+ * shape is invalid. */
+size_t wf_kv_pool_bytes(int n_slots, int chunk_tokens, int n_heads, int head_dim, int dtype);
+
+/* Creates a cache over k_pool and v_pool (each wf_kv_pool_bytes() bytes,
+ * 256-byte aligned). With WF_KV_ZERO_FILL both pools are zeroed on stream;
+ * with WF_KV_ADOPT nothing is enqueued and the caller guarantees that the
+ * padding is zero (pools that a cache already used, e.g. to re-attach a
+ * snapshot with wf_kv_set_table). The table starts empty and every slot is
+ * free. *out receives the handle.
+ * Limits: 1 <= n_slots <= WF_MAX_TABLE, 1 <= chunk_tokens <= 2^20,
+ * 1 <= n_heads <= 1024, head_dim in {64, 128}, dtype WF_F32 or WF_BF16. */
+int wf_kv_cache_create(wf_kv_cache** out, void* k_pool, void* v_pool, int n_slots,
+                       int chunk_tokens, int n_heads, int head_dim, int dtype, int flags,
+                       void* stream);
+
+/* Frees the host handle only (the pools stay the caller's). NULL is accepted. */
+int wf_kv_cache_destroy(wf_kv_cache* kv);
+
+/* Appends a chunk: takes the oldest free slot, enqueues the copy of k and v
+ * (each [chunk_tokens][n_heads][head_dim] in the cache's dtype, 16-byte
+ * aligned) into it and
+ * pushes the slot onto the end of the table. *out_slot (may be NULL) receives
+ * the physical slot. WF_E_FULL when no slot is free. */
+int wf_kv_append(wf_kv_cache* kv, const void* k, const void* v, void* stream, int* out_slot);
+
+/* Refresh: overwrites, in place, the slot of table entry logical_idx
+ * (0 = oldest) with k and v (same layout as append). Attention launched later
+ * on the same stream reads the new values. */
+int wf_kv_refresh(wf_kv_cache* kv, int logical_idx, const void* k, const void* v, void* stream);
+
+/* Pops the n_oldest oldest table entries; their slots become free (appended to
+ * the free list in table order). Host-only; work already enqueued keeps the
+ * table it was launched with. */
+int wf_kv_evict(wf_kv_cache* kv, int n_oldest);
+
+/* Replaces the table with slots[0..n-1] (distinct, each in [0, n_slots)); all
+ * other slots become free in increasing order. Contents are not touched. Used
+ * for non-contiguous layouts and to restore a snapshot. */
+int wf_kv_set_table(wf_kv_cache* kv, const int* slots, int n);
+
+/* Copies up to cap table entries into slots and the table length into *n. */
+int wf_kv_get_table(const wf_kv_cache* kv, int* slots, int cap, int* n);
+
+/* ------------------------------------------------------------------------
+ * 3D rotary embedding, in place on x [n_tokens][n_heads][head_dim] (dtype).
+ * The pages do not describe positional encoding; this call serves the
+ * long-rollout workload and follows one stated convention:
+ *   head_dim = d_t + d_h + d_w (all even); inside each axis segment of width
+ *   d_a the pair (x[o+2i], x[o+2i+1]) rotates by pos_a * theta^(-2i/d_a);
+ *   token u of chunk g (u in frame-major, then row, then column order) sits
+ *   at (frames_per_chunk*g + frame, row, col); chunk g of the block is
+ *   first_global_chunk + token / chunk_tokens, where
+ *   chunk_tokens = frames_per_chunk * grid_h * grid_w.
+ * Angles are fp32 products pos * inv_freq (inv_freq rounded once to fp32);
+ * arithmetic is fp32; bf16 results are rounded to nearest even.
+ * n_tokens must be a multiple of chunk_tokens.
+ * ------------------------------------------------------------------------ */
+int wf_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dtype, int first_global_chunk,
+              int frames_per_chunk, int grid_h, int grid_w, int d_t, int d_h, int d_w, float theta,
+              void* stream);
+
+/* ------------------------------------------------------------------------
+ * Chunk-wise causal attention of one round (the round's hot loop).
+ * q, out: [n_inflight*chunk_tokens][n_heads][head_dim] in the cache dtype;
+ * query chunk j (0 = refresh chunk) reads the first n_hist + j + 1 table
+ * entries, n_hist = table length - n_inflight:
+ *   out[i,h] = sum_k exp(s_ik) v_kh / sum_k exp(s_ik),  s_ik = scale <q_ih, k_kh>
+ *   lse[h][i] = ln sum_k exp(s_ik)          (fp32, layout [n_heads][n_q]; may be NULL)
+ * Accumulation is fp32; for WF_BF16 the softmax weights are rounded to bf16
+ * before the weighted sum of values, and out is rounded to nearest even.
+ * Results are deterministic: bitwise identical run to run, for any physical
+ * slot placement, and unaffected by the contents of later chunks.
+ * Requires 1 <= n_inflight <= table length, scale > 0, q and out 16-byte
+ * aligned.
+ * ------------------------------------------------------------------------ */
+int wf_chunk_causal_attn_fwd(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
+                             void* out, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * int8-QK variant (bf16 caches, head_dim 128). The pages name a
+ * quantized-QK attention backend (SageAttention) in their DiT-only tests
+ * (Abstract) without its internals; this call implements one scheme:
+ *   mean_h = per-(head, channel) mean of all visible keys (fp64 sum, fp32);
+ *   Q and K - mean are quantized per head in blocks of 128 tokens that start
+ *   at every chunk start: s = amax/127 (1 if amax = 0), code =
+ *   clamp(round_half_even(x/s), -127, 127), all decisions in fp32;
+ *   S = int32 dot products of the codes times s_q * s_k * scale; softmax
+ *   fp32; P rounded to bf16; P.V in bf16 with fp32 accumulation.
+ * The mean shift changes no softmax row; lse refers to the unshifted keys
+ * (the kernel adds scale * <q^_i, mean_h>, q^ the dequantized query).
+ * workspace: device memory of wf_attn_i8qk_workspace_bytes() bytes, 256-byte
+ * aligned, caller-owned, overwritten by every call.
+ * ------------------------------------------------------------------------ */
+size_t wf_attn_i8qk_workspace_bytes(const wf_kv_cache* kv, int n_inflight);
+
+int wf_chunk_causal_attn_fwd_i8qk(const void* q, const wf_kv_cache* kv, int n_inflight,
+                                  float scale, void* workspace, void* out, float* lse,
+                                  void* stream);
+
+/* ---- diagnostics ---- */
+const char* wf_status_str(int status); /* static string for a status code      */
+const char* wf_last_error(void);      /* thread-local text of the last failure */
+int wf_version(void);                 /* major*10000 + minor*100 + patch       */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WF_H */

@@ -1,0 +1,112 @@
+"""Helpers for the GPU tests: drive a round through the C ABI binding and compare
+with the fp64 oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle.attention as OA  # noqa: E402
+
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_REL = 5e-3
+F32_MAX_ABS = 1e-4
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this environment")
+    import chunk_causal_dit_amd as wf  # raises if the library is missing: no fallback
+    wf.lib()
+    return wf
+
+
+def torch_dtype(name: str):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def to_dev(a: np.ndarray, dtype) -> torch.Tensor:
+    # inputs are already representable in dtype, so the conversion is exact
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(dtype)
+
+
+def chunks(a: torch.Tensor, C: int):
+    return [a[i * C:(i + 1) * C] for i in range(a.shape[0] // C)]
+
+
+def build_cache(wf, C, H, D, dtype, k_hist, v_hist, k_in, v_in, n_slots=None, table=None):
+    """Fill a cache with history then in-flight chunks (logical order). With a
+    table, the entries are placed in those physical slots via set_table+refresh."""
+    kh, vh = chunks(k_hist, C), chunks(v_hist, C)
+    ki, vi = chunks(k_in, C), chunks(v_in, C)
+    n = len(kh) + len(ki)
+    cache = wf.KVCache(n_slots or n, C, H, D, dtype)
+    if table is None:
+        for k, v in zip(kh + ki, vh + vi):
+            cache.append(k, v)
+    else:
+        cache.set_table(table)
+        for i, (k, v) in enumerate(zip(kh + ki, vh + vi)):
+            cache.refresh(i, k, v)
+    return cache
+
+
+def gpu_round(wf, inp, table=None, n_slots=None, with_lse=True):
+    cfg = inp.cfg
+    dt = torch_dtype(cfg.dtype)
+    C, H, D = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim
+    dev = {k: to_dev(getattr(inp, k), dt) for k in ("q", "k_hist", "v_hist", "k_in", "v_in")}
+    cache = build_cache(wf, C, H, D, dt, dev["k_hist"], dev["v_hist"], dev["k_in"], dev["v_in"],
+                        n_slots=n_slots, table=table)
+    out, lse = wf.chunk_causal_attn_fwd(dev["q"], cache, cfg.n_inflight, cfg.scale, with_lse=with_lse)
+    torch.cuda.synchronize()
+    return out, lse, cache
+
+
+def oracle_round(inp, rows=None, workers=None):
+    cfg = inp.cfg
+    k = np.concatenate([inp.k_hist, inp.k_in])
+    v = np.concatenate([inp.v_hist, inp.v_in])
+    workers = workers or min(16, len(os.sched_getaffinity(0)))
+    return OA.chunk_causal_attention(inp.q, k, v, cfg.n_hist, cfg.chunk_tokens, cfg.scale, rows=rows,
+                                     workers=workers)
+
+
+def error_stats(gpu: np.ndarray, ref: np.ndarray):
+    d = np.abs(gpu.astype(np.float64) - ref)
+    return float(d.max()), float(d.sum() / np.abs(ref).sum())
+
+
+def assert_close(gpu_out, ref_out, dtype: str, what: str = "O"):
+    mx, rel = error_stats(gpu_out, ref_out)
+    print(f"[parity] {what}: max abs {mx:.3e}, mean rel {rel:.3e}", flush=True)
+    assert np.isfinite(gpu_out).all(), f"{what}: non-finite values"
+    if dtype == "f32":
+        assert mx <= F32_MAX_ABS, f"{what}: max abs {mx} > {F32_MAX_ABS}"
+    else:
+        assert mx <= BF16_MAX_ABS, f"{what}: max abs {mx} > {BF16_MAX_ABS}"
+        assert rel <= BF16_MEAN_REL, f"{what}: mean rel {rel} > {BF16_MEAN_REL}"
+    return mx, rel
+
+
+def boundary_rows(C: int, N: int, n_sample: int, seed: int, tile: int = 256):
+    """Sampled query rows: chunk edges, query-tile edges, the ragged tail, plus random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for j in range(N):
+        base = j * C
+        for r in (0, 1, 31, 32, C - 1, C - 2):
+            if 0 <= r < C:
+                rows.add(base + r)
+        for t in range(tile, C, tile):
+            rows.update({base + t - 1, base + t})
+        rows.update(int(base + x) for x in rng.integers(0, C, size=n_sample))
+    return np.array(sorted(rows))
