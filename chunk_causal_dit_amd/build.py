@@ -29,15 +29,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source to an object, then link libwf.so. Returns its path."""
+def build(verbose: bool = False, jobs: int = 4, defines=(), out: str = LIB) -> str:
+    """Compile every source to an object, then link the library (libwf.so by
+    default). ``defines`` are extra -D flags (compile-time kernel variants).
+    Returns the library path."""
     cc = hipcc()
-    obj_dir = os.path.join(HERE, "_build")
+    tag = "_".join(d.replace("=", "") for d in defines)
+    obj_dir = os.path.join(HERE, "_build" + ("_" + tag if tag else ""))
     os.makedirs(obj_dir, exist_ok=True)
     common = [
         "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"-I{INCLUDE}", f"-I{CSRC}",
         "-Wall", "-Wno-unused-function",
-    ]
+    ] + [f"-D{d}" for d in defines]
     hip_flags = [
         f"--offload-arch={ARCH}", "-x", "hip",
         # no packed-FP32 instructions in device code
@@ -63,15 +66,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         if len(procs) >= jobs:
             _drain(procs)
     _drain(procs)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     link = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(link), flush=True)
-    out = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
-    if out.returncode != 0:
-        raise RuntimeError("link failed:\n" + out.stdout.decode(errors="replace"))
-    os.replace(tmp, LIB)
-    return LIB
+    res = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stdout.decode(errors="replace"))
+    os.replace(tmp, out)
+    return out
 
 
 def _drain(procs):

@@ -11,22 +11,25 @@
 //
 // Kernel structure (one workgroup = NW waves = NW*32 query rows of one chunk
 // and one head; grid ordered longest-first):
-//   * Each wave keeps its 32 query rows as the stationary MFMA B operand.
-//   * K and V^T tiles of 64 keys are staged global -> registers -> LDS with a
-//     double buffer, one barrier per tile; the next tile's global loads are in
-//     flight while the current tile is consumed.
+//   * Each wave keeps its 32 query rows in registers as the stationary MFMA B
+//     operand.
+//   * Key tiles (64 keys) are stored in the cache as LDS images (see
+//     kv_cache.hip) and copied HBM -> LDS with global_load_lds_dwordx4: no
+//     staging registers, no LDS write instructions. Three K stages and three V
+//     stages; the copies of K(t+2) and V(t+1) are in flight while tile t is
+//     consumed.
 //   * S^T = K Q^T on MFMA: lane (q, half) of the 32x32 output holds one query
 //     and 16 keys, so the softmax row statistics need one cross-half exchange.
 //     The K rows are read in a permuted order (key_of_arow) so that the 16 keys
 //     of a lane come out as two runs of 8 consecutive keys, which is exactly
 //     the B-operand layout of the next contraction.
 //   * O^T += V^T P^T on MFMA, P taken straight from registers (bf16 for the
-//     bf16 path). V is stored transposed (key-contiguous) in the cache, so the
-//     A operand is one 16-byte LDS read.
+//     bf16 path).
 //   * Online softmax in the exp2 domain with a lazily moved reference max:
 //     the accumulators are rescaled only when a row's max grows by more than
 //     2^8, which keeps weights <= 256 and the result exact up to rounding.
 #include <cmath>
+#include <type_traits>
 
 #include "wf_internal.h"
 
@@ -37,6 +40,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int KT = 64;  // keys per tile
 constexpr float kLn2 = 0.69314718055994531f;
@@ -51,14 +55,51 @@ __device__ __forceinline__ int key_of_arow(int i) {
 }
 __device__ __forceinline__ int key_of_elem(int hh, int r) { return ((r >> 3) << 4) + (hh << 3) + (r & 7); }
 
-// XOR swizzles of 16-byte pieces inside an LDS row (low 3 bits only). The
-// K swizzle gives the 8 rows read together by a lane group (rows key_of_arow)
-// 8 distinct pieces; the V^T swizzle does the same for 8 consecutive rows.
-__device__ __forceinline__ int swz_k(int row) { return (row & 7) ^ ((row >> 1) & 4); }
-__device__ __forceinline__ int swz_v(int row) { return row & 7; }
-
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// max / sum over the two halves of a row with one v_permlane32_swap: for lane
+// l < 32 it returns (x[l], x[l+32]), for l >= 32 (x[l-32], x[l]).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Wait until at most N of this wave's vector-memory operations are still in
+// flight (the LDS copies of the newest step), finish this wave's LDS reads,
+// then meet the other waves. Unlike __syncthreads() this does not drain the
+// copies that are meant to stay in flight across the barrier.
+#define WF_WAIT_VM_BARRIER(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N <= 8, "unsupported wait count");
+  if constexpr (N == 0) WF_WAIT_VM_BARRIER(0);
+  if constexpr (N == 1) WF_WAIT_VM_BARRIER(1);
+  if constexpr (N == 2) WF_WAIT_VM_BARRIER(2);
+  if constexpr (N == 3) WF_WAIT_VM_BARRIER(3);
+  if constexpr (N == 4) WF_WAIT_VM_BARRIER(4);
+  if constexpr (N == 6) WF_WAIT_VM_BARRIER(6);
+  if constexpr (N == 8) WF_WAIT_VM_BARRIER(8);
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Keep a block's results on its side of the next barrier: the compiler may
+// not sink the instructions producing these registers past this point (volatile
+// asm statements keep their order, and the barrier is one).
+__device__ __forceinline__ void pin_scores(f32x16& a, f32x16& b) { asm volatile("" : "+v"(a), "+v"(b)); }
+__device__ __forceinline__ void pin_weights(bf16x8 (&p)[4]) {
+  asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
+}
 
 struct Work {
   int j, h, qt;
@@ -76,86 +117,125 @@ __device__ __forceinline__ Work decode_block(int b, int N, int H, int T) {
   return w;
 }
 
+// Tile images: K [D/E pieces][64 keys][16 B], V [64/E pieces][D dims][16 B].
 template <typename E, int D, int NW>
 struct Geo {
   static constexpr int ES = sizeof(E);
-  static constexpr int CK = D * ES / 16;   // 16-byte pieces per K row
-  static constexpr int CV = KT * ES / 16;  // 16-byte pieces per V^T row
-  static constexpr int K_BYTES = KT * D * ES;
-  static constexpr int STAGE = 2 * K_BYTES;  // K tile + V^T tile
-  static constexpr int LDS = 2 * STAGE;      // double buffer
+  static constexpr int TILE = KT * D * ES;      // bytes of one K (or V) tile image
+  static constexpr int KPS = KT * 16;           // K image: bytes per piece (64 keys)
+  static constexpr int VPS = D * 16;            // V image: bytes per piece (D dims)
+  static constexpr int NSTAGE = 3;
+  static constexpr int LDS = 2 * NSTAGE * TILE; // three K stages, then three V stages
   static constexpr int NT = NW * 64;
-  static constexpr int NK = KT * CK / NT;
-  static constexpr int NV = D * CV / NT;
-  static_assert(NK * NT == KT * CK && NV * NT == D * CV, "tile must split evenly over the threads");
-  static_assert(CK % 8 == 0 && CV % 8 == 0, "swizzles need >= 8 pieces per row");
+  static constexpr int COPIES = TILE / 1024;    // 1 KB copy instructions per tile image
+  static constexpr int CPW = COPIES / NW;       // per wave, per tensor
+  static_assert(CPW * NW == COPIES, "tile copies must split evenly over the waves");
 };
 
-// Global -> register -> LDS staging of one K tile and one V^T tile.
+// Direct HBM -> LDS copy of one tile image: wave w issues copies w, w+NW, ...
 template <typename G>
-struct Stager {
-  u32x4 k[G::NK];
-  u32x4 v[G::NV];
-  __device__ __forceinline__ void load(const char* kb, const char* vb, size_t v_row_bytes, int tid) {
+__device__ __forceinline__ void copy_tile(const char* src, char* lds_dst, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < G::NK; ++i) {
-      const int id = tid + i * G::NT, row = id / G::CK, c = id % G::CK;
-      k[i] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * (G::CK * 16) + c * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < G::NV; ++i) {
-      const int id = tid + i * G::NT, d = id / G::CV, c = id % G::CV;
-      v[i] = *reinterpret_cast<const u32x4*>(vb + (size_t)d * v_row_bytes + c * 16);
-    }
+  for (int i = 0; i < G::CPW; ++i) {
+    const int c = wave + i * (G::COPIES / G::CPW);
+    __builtin_amdgcn_global_load_lds(src + c * 1024 + lane * 16, (LDS_AS void*)(lds_dst + c * 1024), 16, 0, 0);
   }
-  __device__ __forceinline__ void store(char* stage, int tid) const {
-#pragma unroll
-    for (int i = 0; i < G::NK; ++i) {
-      const int id = tid + i * G::NT, row = id / G::CK, c = id % G::CK;
-      *reinterpret_cast<u32x4*>(stage + row * (G::CK * 16) + ((c ^ swz_k(row)) << 4)) = k[i];
-    }
-    char* vs = stage + G::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < G::NV; ++i) {
-      const int id = tid + i * G::NT, d = id / G::CV, c = id % G::CV;
-      *reinterpret_cast<u32x4*>(vs + d * (G::CV * 16) + ((c ^ swz_v(d)) << 4)) = v[i];
-    }
-  }
-};
+}
 
-// Addresses of key tile kt of logical chunk cl for head h.
-template <typename G, int D>
+// Addresses of key tile t (logical chunk t / ktc, tile t % ktc) for head h.
 struct TileSrc {
   const char* kpool;
   const char* vpool;
-  size_t slot_bytes, khead, vhead;
+  size_t slot_bytes, head_off;
+  int tile_bytes, ktc;
   const int* slots;
-  __device__ __forceinline__ void at(int cl, int kt, const char*& kb, const char*& vb) const {
-    const size_t base = (size_t)slots[cl] * slot_bytes;
-    kb = kpool + base + khead + (size_t)kt * (KT * D * G::ES);
-    vb = vpool + base + vhead + (size_t)kt * (KT * G::ES);
+  __device__ __forceinline__ size_t off(int t) const {
+    const int cl = t / ktc;
+    return (size_t)slots[cl] * slot_bytes + head_off + (size_t)(t - cl * ktc) * tile_bytes;
   }
 };
 
-extern __shared__ __attribute__((aligned(16))) char g_smem[];
+extern __shared__ __attribute__((aligned(1024))) char g_smem[];
 
 // ---------------------------------------------------------------- bf16
-template <int D, int NW>
+// Work of one wave on key tile t is split into an MFMA block and a VALU block:
+//   M_t = { O^T += V(t-1)^T P(t-1)^T ;  S^T = K(t) Q^T }   (two independent contractions)
+//   V_t = { online softmax of S -> P(t) }
+// Step t: start the copies of K(t+2) and V(t+1), run M_t and V_t, wait for the
+// copies of the previous step (K(t+1), V(t)), barrier. K(t) lives in K stage
+// t%3 from step t-2 to step t, V(t) in V stage t%3 from step t-1 to step t+1,
+// so no stage is overwritten while a wave can still read it.
+//
+// PINGPONG = true: waves 0-3 and 4-7 (one of each per SIMD) run half a step
+// apart, each half-step ending with a barrier, so that on every SIMD one wave
+// feeds the matrix cores while the other runs the softmax.
+#ifndef WF_ATTN_PINGPONG
+#define WF_ATTN_PINGPONG 1
+#endif
+#ifndef WF_ATTN_LDS_DEPTH
+#define WF_ATTN_LDS_DEPTH 4
+#endif
+#ifndef WF_ATTN_SETPRIO
+#define WF_ATTN_SETPRIO 0
+#endif
+#ifndef WF_ATTN_LEAD_GROUP
+#define WF_ATTN_LEAD_GROUP 1
+#endif
+
+template <int D, int NW, bool PINGPONG>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p) {
+  static_assert(NW == 8, "8 waves: two per SIMD");
   using G = Geo<__bf16, D, NW>;
   constexpr int KS = D / 16;  // MFMA steps over head_dim (16 per step)
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   char* smem = g_smem;
 
   const Work w = decode_block(blockIdx.x, p.n_inflight, p.n_heads, p.q_tiles);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = (wave >> 2) ^ WF_ATTN_LEAD_GROUP;  // group 0 leads by half a step
   const int qi = lane & 31, hh = lane >> 5;
-  const int C = p.chunk_tokens, H = p.n_heads, s_pad = p.s_pad;
+  const int C = p.chunk_tokens, H = p.n_heads;
   const int wrow = w.qt * (NW * 32) + wave * 32;
   const bool wave_on = wrow < C;
   const int row = wrow + qi;
   const bool row_ok = row < C;
   const size_t qoff = (((size_t)w.j * C + row) * H + w.h) * D;
+
+  const int ktc = p.key_tiles;
+  const int n_vis = p.n_hist + w.j + 1;  // visible logical chunks
+  const int n_iter = n_vis * ktc;
+  const char* kpool = static_cast<const char*>(p.k_pool);
+  const char* vpool = static_cast<const char*>(p.v_pool);
+  const size_t slot_bytes = (size_t)p.slot_elems * G::ES;
+  const size_t head_off = (size_t)w.h * p.s_pad * D * G::ES;
+  // Wave-uniform cursor over the tiles in visiting order (chunk by chunk), so
+  // the loop needs no divisions: byte offset of the tile in a pool.
+  struct Cursor {
+    int cl, kt;
+    size_t off;
+  };
+  auto cursor_at = [&](int t) {
+    Cursor c;
+    c.cl = t / ktc;
+    c.kt = t - c.cl * ktc;
+    c.off = (size_t)p.slots[c.cl] * slot_bytes + head_off + (size_t)c.kt * G::TILE;
+    return c;
+  };
+  auto advance = [&](Cursor& c) {
+    c.off += G::TILE;
+    if (++c.kt == ktc) {
+      c.kt = 0;
+      if (++c.cl < n_vis) c.off = (size_t)p.slots[c.cl] * slot_bytes + head_off;
+    }
+  };
+  auto kst = [&](int r) { return smem + r * G::TILE; };                  // K stage r
+  auto vst = [&](int r) { return smem + (G::NSTAGE + r) * G::TILE; };   // V stage r
+
+  // prologue copies: K(0) -> K stage 0, K(1) -> K stage 1, V(0) -> V stage 0
+  copy_tile<G>(kpool + cursor_at(0).off, kst(0), wave, lane);
+  if (n_iter > 1) copy_tile<G>(kpool + cursor_at(1).off, kst(1), wave, lane);
+  copy_tile<G>(vpool + cursor_at(0).off, vst(0), wave, lane);
 
   // Stationary B operand: this lane's query row, half hh of head_dim.
   bf16x8 qop[KS];
@@ -168,125 +248,196 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
       __builtin_memcpy(&qop[k], &raw, 16);
     }
   }
-
-  TileSrc<G, D> src{static_cast<const char*>(p.k_pool), static_cast<const char*>(p.v_pool),
-                    (size_t)p.slot_elems * G::ES, (size_t)w.h * s_pad * D * G::ES,
-                    (size_t)w.h * D * s_pad * G::ES, p.slots};
-  const size_t v_row_bytes = (size_t)s_pad * G::ES;
-  const int ktc = p.key_tiles;
-  const int n_iter = (p.n_hist + w.j + 1) * ktc;
-
-  Stager<G> st;
-  {
-    const char *kb, *vb;
-    src.at(0, 0, kb, vb);
-    st.load(kb, vb, v_row_bytes, tid);
-    st.store(smem, tid);
+  {  // V stage of "tile -1" (read once, multiplied by P = 0) must hold finite values
+    u32x4* z = reinterpret_cast<u32x4*>(vst(G::NSTAGE - 1));
+    for (int i = tid; i < G::TILE / 16; i += G::NT) z[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  __syncthreads();
+  wait_vm_barrier<0>();
 
   f32x16 o[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  float m_ref = -INFINITY;  // reference max (log2 domain) of this lane's query row
-  float lsum = 0.f;         // this half's share of the row sum of weights
+  f32x16 s[2];
+  bf16x8 pk[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pk[kk][e] = (__bf16)0.f;
+  float m_ref = -INFINITY;                  // reference max (log2 domain) of this lane's query row
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};     // this half's share of the row sum of weights
   const float sl2e = p.scale_log2e;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // per-lane operand offsets inside a stage; every op adds a compile-time constant
+  const int k_lane = key_of_arow(qi) * 16 + hh * KS * G::KPS;
+  const int v_lane = qi * 16 + hh * G::VPS;
 
-  int cl = 0, kt = 0;
-  for (int it = 0; it < n_iter; ++it) {
+  // MFMA block with an explicit operand pipeline: LDS reads run DEPTH
+  // operands ahead of the MFMAs in one straight-line region. Op i < NPV is a
+  // P.V step (kk = i / DB, d = i % DB); op i >= NPV a Q.K step (k, b).
+  constexpr int DEPTH = WF_ATTN_LDS_DEPTH;
+  constexpr int NPV = 4 * DB, NQK = 2 * KS;
+  auto mrun = [&](const char* vs, const char* ks, auto has_pv, auto has_qk) {
+    constexpr bool PV = decltype(has_pv)::value, QK = decltype(has_qk)::value;
+    constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NPV + NQK : NPV;
+    auto rd = [&](auto ic) -> bf16x8 {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < NPV)
+        return *reinterpret_cast<const bf16x8*>(vs + (i / DB) * 2 * G::VPS + (i % DB) * 32 * 16);
+      else
+        return *reinterpret_cast<const bf16x8*>(ks + ((i - NPV) / 2) * G::KPS + ((i - NPV) % 2) * 32 * 16);
+    };
+    auto mm = [&](auto ic, const bf16x8& a) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < NPV) {
+        o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[i / DB], o[i % DB], 0, 0, 0);
+      } else {
+        constexpr int j = i - NPV;
+        if constexpr (j < 2)
+          s[j % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[j / 2], f32x16{}, 0, 0, 0);
+        else
+          s[j % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[j / 2], s[j % 2], 0, 0, 0);
+      }
+    };
+    bf16x8 buf[DEPTH];
+    static_for<0, DEPTH>([&](auto q) {
+      constexpr int i = I0 + decltype(q)::value;
+      if constexpr (i < I1) buf[decltype(q)::value] = rd(std::integral_constant<int, i>{});
+    });
+    static_for<I0, I1>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const bf16x8 a = buf[(i - I0) % DEPTH];
+      if constexpr (i + DEPTH < I1) buf[(i - I0) % DEPTH] = rd(std::integral_constant<int, i + DEPTH>{});
+      mm(ic, a);
+    });
+    // keep the pattern: DEPTH reads, then {MFMA, read} pairs, then the tail MFMAs
+    constexpr int N = I1 - I0;
+    __builtin_amdgcn_sched_group_barrier(0x100, DEPTH < N ? DEPTH : N, 0);
+    static_for<0, N>([&](auto ic) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (decltype(ic)::value + DEPTH < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+  };
+  // One fused MFMA block every step: at step 0 the P.V half multiplies P = 0
+  // with the zero-filled V stage of "tile -1"; at step n_iter the Q.K half
+  // computes scores that are never used. r = t % 3 is the K stage of tile t.
+  auto mblock = [&](int r) {
+    const int rv = r == 0 ? G::NSTAGE - 1 : r - 1;  // V stage of tile t-1
+    if (WF_ATTN_SETPRIO == 1) __builtin_amdgcn_s_setprio(1);  // the matrix-core feeder wins issue ties
+    mrun(vst(rv) + v_lane, kst(r) + k_lane, std::true_type{}, std::true_type{});
+    if (WF_ATTN_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto vblock = [&](int kt) {  // online softmax of a tile; kt = its index inside its chunk
+    if (WF_ATTN_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
     const int valid = min(KT, C - kt * KT);
-    int ncl = cl, nkt = kt + 1;
-    if (nkt == ktc) {
-      nkt = 0;
-      ++ncl;
-    }
-    const bool more = it + 1 < n_iter;
-    if (more) {
-      const char *kb, *vb;
-      src.at(ncl, nkt, kb, vb);
-      st.load(kb, vb, v_row_bytes, tid);
-    }
-    const char* ks = smem + (it & 1) * G::STAGE;
-    if (wave_on) {
-      // S^T = K Q^T for 64 keys x 32 queries
-      f32x16 s[2];
+    if (valid < KT) {  // zero padding past the chunk end takes no weight
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int r = 32 * b + key_of_arow(qi);
-          const int c = hh * KS + k;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + r * (G::CK * 16) + ((c ^ swz_k(r)) << 4));
-          s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[k], s[b], 0, 0, 0);
-        }
-      }
-      if (valid < KT) {  // zero padding past the chunk end takes no weight
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (32 * b + key_of_elem(hh, e) >= valid) s[b][e] = -INFINITY;
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
-      mx = fmaxf(mx, xor32(mx));
-      const float tmax = mx * sl2e;
-      if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleLog2)) {
-        const float mn = fmaxf(m_ref, tmax);
-        const float alpha = fast_exp2(m_ref - mn);
-        m_ref = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int d = 0; d < DB; ++d)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-      }
-      const float nm = -m_ref;
-      bf16x8 pk[4];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) pk[2 * b + (e >> 3)][e & 7] = (__bf16)fast_exp2(fmaf(s[b][e], sl2e, nm));
-      // row sum of the weights actually used (bf16-rounded)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-        {
-          const bf16x2 pr = {pk[kk][2 * e], pk[kk][2 * e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
-        }
-      // O^T += V^T P^T
-      const char* vs = ks + G::K_BYTES;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const int r = 32 * d + qi;
-          const int c = 2 * kk + hh;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + r * (G::CV * 16) + ((c ^ swz_v(r)) << 4));
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], o[d], 0, 0, 0);
-        }
-      }
+        for (int e = 0; e < 16; ++e)
+          if (32 * b + key_of_elem(hh, e) >= valid) s[b][e] = -INFINITY;
     }
-    if (more) st.store(smem + ((it + 1) & 1) * G::STAGE, tid);
-    __syncthreads();
-    cl = ncl;
-    kt = nkt;
+    // row max as four independent chains, then the other half of the row
+    float m4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      m4[c] = fmaxf(s[c >> 1][(c & 1) * 8], s[c >> 1][(c & 1) * 8 + 1]);
+#pragma unroll
+      for (int e = 2; e < 8; ++e) m4[c] = fmaxf(m4[c], s[c >> 1][(c & 1) * 8 + e]);
+    }
+    float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+    const float tmax = mx * sl2e;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleLog2)) {
+      const float mn = fmaxf(m_ref, tmax);
+      const float alpha = fast_exp2(m_ref - mn);
+      m_ref = mn;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lsum[c] *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+    }
+    const float nm = -m_ref;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pk[2 * b + (e >> 3)][e & 7] = (__bf16)fast_exp2(fmaf(s[b][e], sl2e, nm));
+    // row sum of the weights actually used (bf16-rounded), four accumulators
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {pk[kk][2 * e], pk[kk][2 * e + 1]};
+        lsum[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[kk], false);
+      }
+    if (WF_ATTN_SETPRIO == 2) __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Copies started in step t: K(t+2) into K stage (t+2)%3, V(t+1) into V stage
+  // (t+1)%3; then wait for the copies of step t-1 and meet the other waves.
+  Cursor ck = cursor_at(n_iter > 2 ? 2 : 0), cv = cursor_at(n_iter > 1 ? 1 : 0);
+  auto copies_and_wait = [&](int t, int r) {
+    const bool dk = t + 2 < n_iter, dv = t + 1 < n_iter;
+    const int r1 = r == G::NSTAGE - 1 ? 0 : r + 1, r2 = r1 == G::NSTAGE - 1 ? 0 : r1 + 1;
+    if (dk) {
+      copy_tile<G>(kpool + ck.off, kst(r2), wave, lane);
+      advance(ck);
+    }
+    if (dv) {
+      copy_tile<G>(vpool + cv.off, vst(r1), wave, lane);
+      advance(cv);
+    }
+    constexpr int per = G::CPW;  // copy instructions per tensor and wave
+    if (dk && dv)
+      wait_vm_barrier<2 * per>();
+    else if (dv)
+      wait_vm_barrier<per>();
+    else
+      wait_vm_barrier<0>();
+  };
+
+  if (!wave_on) {  // a wave past the chunk end still copies and meets every barrier
+    for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
+      if (PINGPONG) lds_barrier();
+      copies_and_wait(t, r);
+    }
+  } else if (!PINGPONG || grp == 0) {
+    // in-phase order (and ping-pong group 0): M_t, [barrier], V_t, copies + barrier
+    int vkt = 0;
+    for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
+      mblock(r);
+      if (PINGPONG) {
+        pin_scores(s[0], s[1]);
+        lds_barrier();
+      }
+      if (t < n_iter) {
+        vblock(vkt);
+        vkt = vkt + 1 == ktc ? 0 : vkt + 1;
+      }
+      pin_weights(pk);
+      copies_and_wait(t, r);
+    }
+  } else {
+    // ping-pong group 1, half a step behind: V_{t-1}, barrier, M_t, copies + barrier
+    int vkt = 0;
+    for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
+      if (t >= 1) {
+        vblock(vkt);
+        vkt = vkt + 1 == ktc ? 0 : vkt + 1;
+      }
+      pin_weights(pk);
+      lds_barrier();
+      mblock(r);
+      pin_scores(s[0], s[1]);
+      copies_and_wait(t, r);
+    }
   }
 
   if (wave_on) {
-    const float lt = lsum + xor32(lsum);
+    const float lt = halves_sum((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
     const float inv = 1.0f / lt;
     if (row_ok) {
       __bf16* orow = static_cast<__bf16*>(p.o) + qoff;
@@ -307,9 +458,305 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
   }
 }
 
+
+// ---------------------------------------------------------------- bf16, one wave per SIMD
+// Each wave owns 64 query rows as two halves A and B (32 rows each). Per half
+// the work on key tile t is Q_X(t) (MFMA: S = K Q^T), S_X(t) (softmax: S -> P)
+// and P_X(t) (MFMA: O += V^T P^T), strictly in that order. The two halves are
+// offset so that every slot pairs one half's MFMAs with the other half's
+// softmax:
+//   slot 2t+2:  MFMA { P_A(t), Q_A(t+1) }   VALU { S_B(t) }
+//   slot 2t+3:  MFMA { P_B(t), Q_B(t+1) }   VALU { S_A(t+1) }
+// Every register buffer is single (a half's S is overwritten only after its
+// softmax read it, its P only after its P.V read it). Inside a slot the
+// softmax's exp / bf16 / row-sum part is interleaved about three VALU per
+// MFMA; its row max, rescale test and rare rescale run just before the slot.
+// Slots 2t+2 and 2t+3 read V(t) and K(t+1); LDS copies and the one barrier per
+// step follow the three-stage schedule above.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_bf16_w1_kernel(wf::AttnParams p) {
+  constexpr int NW = 4;
+  using G = Geo<__bf16, D, NW>;
+  constexpr int KS = D / 16;  // MFMA steps over head_dim
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  char* smem = g_smem;
+
+  const Work w = decode_block(blockIdx.x, p.n_inflight, p.n_heads, p.q_tiles);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qi = lane & 31, hh = lane >> 5;
+  const int C = p.chunk_tokens, H = p.n_heads;
+  const int wrow = w.qt * (NW * 64) + wave * 64;
+  const bool wave_on = wrow < C;
+  const int rowA = wrow + qi, rowB = wrow + 32 + qi;
+  const bool okA = rowA < C, okB = rowB < C;
+
+  const int ktc = p.key_tiles;
+  const int n_vis = p.n_hist + w.j + 1;
+  const int n_iter = n_vis * ktc;
+  const char* kpool = static_cast<const char*>(p.k_pool);
+  const char* vpool = static_cast<const char*>(p.v_pool);
+  const size_t slot_bytes = (size_t)p.slot_elems * G::ES;
+  const size_t head_off = (size_t)w.h * p.s_pad * D * G::ES;
+  struct Cursor {
+    int cl, kt;
+    size_t off;
+  };
+  auto cursor_at = [&](int t) {
+    Cursor c;
+    c.cl = t / ktc;
+    c.kt = t - c.cl * ktc;
+    c.off = (size_t)p.slots[c.cl] * slot_bytes + head_off + (size_t)c.kt * G::TILE;
+    return c;
+  };
+  auto advance = [&](Cursor& c) {
+    c.off += G::TILE;
+    if (++c.kt == ktc) {
+      c.kt = 0;
+      if (++c.cl < n_vis) c.off = (size_t)p.slots[c.cl] * slot_bytes + head_off;
+    }
+  };
+  auto kst = [&](int r) { return smem + r * G::TILE; };
+  auto vst = [&](int r) { return smem + (G::NSTAGE + r) * G::TILE; };
+
+  copy_tile<G>(kpool + cursor_at(0).off, kst(0), wave, lane);
+  if (n_iter > 1) copy_tile<G>(kpool + cursor_at(1).off, kst(1), wave, lane);
+  copy_tile<G>(vpool + cursor_at(0).off, vst(0), wave, lane);
+
+  bf16x8 qA[KS], qB[KS];
+  {
+    const size_t qoffA = (((size_t)w.j * C + rowA) * H + w.h) * D + hh * (D / 2);
+    const size_t qoffB = (((size_t)w.j * C + rowB) * H + w.h) * D + hh * (D / 2);
+    const u32x4* pa = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) + qoffA);
+    const u32x4* pb = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) + qoffB);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      u32x4 ra = {0u, 0u, 0u, 0u}, rb = {0u, 0u, 0u, 0u};
+      if (okA) ra = pa[k];
+      if (okB) rb = pb[k];
+      __builtin_memcpy(&qA[k], &ra, 16);
+      __builtin_memcpy(&qB[k], &rb, 16);
+    }
+  }
+  wait_vm_barrier<0>();
+
+  f32x16 oA[DB], oB[DB], sA[2], sB[2];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oA[d][e] = oB[d][e] = 0.f;
+  // Register classes: the stationary Q operands and the O accumulators live in
+  // AGPRs (MFMA reads B and C from there), leaving the VGPRs to S, P and the
+  // softmax.
+#pragma unroll
+  for (int k = 0; k < KS; ++k) asm volatile("" : "+a"(qA[k]), "+a"(qB[k]));
+#pragma unroll
+  for (int d = 0; d < DB; ++d) asm volatile("" : "+a"(oA[d]), "+a"(oB[d]));
+  bf16x8 pA[4], pB[4];
+  float mA = -INFINITY, mB = -INFINITY;
+  float lA[2] = {0.f, 0.f}, lB[2] = {0.f, 0.f};
+  const float sl2e = p.scale_log2e;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int k_lane = key_of_arow(qi) * 16 + hh * KS * G::KPS;
+  const int v_lane = qi * 16 + hh * G::VPS;
+  constexpr int DEPTH = 4;
+
+  // softmax part 1 (before the slot): padding mask, row max, rare rescale
+  auto sm_pre = [&](f32x16 (&sv)[2], float& m, float (&l)[2], f32x16 (&ov)[DB], int kt) {
+    const int valid = min(KT, C - kt * KT);
+    if (valid < KT) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * b + key_of_elem(hh, e) >= valid) sv[b][e] = -INFINITY;
+    }
+    float m4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      m4[c] = fmaxf(sv[c >> 1][(c & 1) * 8], sv[c >> 1][(c & 1) * 8 + 1]);
+#pragma unroll
+      for (int e = 2; e < 8; ++e) m4[c] = fmaxf(m4[c], sv[c >> 1][(c & 1) * 8 + e]);
+    }
+    const float tmax = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * sl2e;
+    if (__builtin_amdgcn_ballot_w64(tmax > m + kRescaleLog2)) {
+      const float mn = fmaxf(m, tmax);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l[0] *= alpha;
+      l[1] *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ov[d][e] *= alpha;
+        asm volatile("" : "+a"(ov[d]));  // back to the accumulator registers inside the branch
+      }
+    }
+  };
+  // A slot: the MFMAs of half X (P.V of tile t if PV, then Q.K of tile t+1
+  // if QK) interleaved unit by unit with the exp part of the softmax of half Y
+  // (if SM). Unit i = { LDS read for op i+DEPTH, MFMA op i, softmax element i:
+  // p = exp2(s*scale*log2e - m); every odd element also packs the pair to bf16
+  // and adds it to the row sum }. The sched_group_barrier sequence at the end
+  // pins exactly this order. Op i < NPV: P.V step (kk = i / DB, d = i % DB);
+  // otherwise Q.K step (k, b).
+  constexpr int NPV = 4 * DB, NQK = 2 * KS;
+  auto slot = [&](const char* vs, const char* ks, f32x16 (&ov)[DB], const bf16x8 (&pv)[4], f32x16 (&sv)[2],
+                  const bf16x8 (&qv)[KS], const f32x16 (&sy)[2], float my, float (&ly)[2], bf16x8 (&py)[4],
+                  auto has_pv, auto has_qk, auto has_sm) {
+    constexpr bool PV = decltype(has_pv)::value, QK = decltype(has_qk)::value, SM = decltype(has_sm)::value;
+    constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NPV + NQK : NPV, NM = I1 - I0;
+    constexpr int NU = SM ? (NM > 32 ? NM : 32) : NM;  // units: MFMAs and softmax elements
+    auto rd = [&](auto ic) -> bf16x8 {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < NPV)
+        return *reinterpret_cast<const bf16x8*>(vs + (i / DB) * 2 * G::VPS + (i % DB) * 32 * 16);
+      else
+        return *reinterpret_cast<const bf16x8*>(ks + ((i - NPV) / 2) * G::KPS + ((i - NPV) % 2) * 32 * 16);
+    };
+    auto mm = [&](auto ic, const bf16x8& a) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < NPV) {
+        ov[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[i / DB], ov[i % DB], 0, 0, 0);
+      } else {
+        constexpr int j = i - NPV;
+        if constexpr (j < 2)
+          sv[j % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[j / 2], f32x16{}, 0, 0, 0);
+        else
+          sv[j % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[j / 2], sv[j % 2], 0, 0, 0);
+      }
+    };
+    const float nm = -my;
+    float pprev = 0.f;
+    bf16x8 buf[DEPTH];
+    static_for<0, DEPTH>([&](auto q) {
+      constexpr int i = I0 + decltype(q)::value;
+      if constexpr (i < I1) buf[decltype(q)::value] = rd(std::integral_constant<int, i>{});
+    });
+    static_for<0, NU>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < NM) {
+        constexpr int i = I0 + u;
+        const bf16x8 a = buf[u % DEPTH];
+        if constexpr (i + DEPTH < I1) buf[u % DEPTH] = rd(std::integral_constant<int, i + DEPTH>{});
+        mm(std::integral_constant<int, i>{}, a);
+      }
+      if constexpr (SM && u < 32) {
+        constexpr int b = u / 16, e = u % 16;
+        const float pe = fast_exp2(fmaf(sy[b][e], sl2e, nm));
+        if constexpr (u & 1) {
+          const bf16x2 pr = {(__bf16)pprev, (__bf16)pe};
+          py[2 * b + (e >> 3)][(e & 7) - 1] = pr[0];
+          py[2 * b + (e >> 3)][e & 7] = pr[1];
+          ly[(u >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ly[(u >> 1) & 1], false);
+        } else {
+          pprev = pe;
+        }
+      }
+    });
+    // results stay inside the slot (no sinking into the next block); S in VGPRs
+    if constexpr (QK) pin_scores(sv[0], sv[1]);
+    if constexpr (SM) {
+      pin_weights(py);
+      asm volatile("" : "+v"(ly[0]), "+v"(ly[1]));
+    }
+    // pin the unit order
+    __builtin_amdgcn_sched_group_barrier(0x100, DEPTH < NM ? DEPTH : NM, 0);
+    static_for<0, NU>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < NM) {
+        if constexpr (u + DEPTH < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      if constexpr (SM && u < 32) __builtin_amdgcn_sched_group_barrier(0x002, (u & 1) ? 4 : 2, 0);
+    });
+  };
+
+  Cursor ck = cursor_at(n_iter > 2 ? 2 : 0), cv = cursor_at(n_iter > 1 ? 1 : 0);
+  auto copies_and_wait = [&](int t, int r) {
+    const bool dk = t + 2 < n_iter, dv = t + 1 < n_iter;
+    const int r1 = r == G::NSTAGE - 1 ? 0 : r + 1, r2 = r1 == G::NSTAGE - 1 ? 0 : r1 + 1;
+    if (dk) {
+      copy_tile<G>(kpool + ck.off, kst(r2), wave, lane);
+      advance(ck);
+    }
+    if (dv) {
+      copy_tile<G>(vpool + cv.off, vst(r1), wave, lane);
+      advance(cv);
+    }
+    constexpr int per = G::CPW;
+    if (dk && dv)
+      wait_vm_barrier<2 * per>();
+    else if (dv)
+      wait_vm_barrier<per>();
+    else
+      wait_vm_barrier<0>();
+  };
+  auto next_r = [](int r) { return r == G::NSTAGE - 1 ? 0 : r + 1; };
+  auto next_kt = [&](int kt) { return kt + 1 == ktc ? 0 : kt + 1; };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  if (!wave_on) {
+    for (int t = 0, r = 0; t < n_iter; ++t, r = next_r(r)) copies_and_wait(t, r);
+  } else {
+    // step 0: slot 0 = Q_A(0); slot 1 = Q_B(0) with S_A(0)
+    slot(nullptr, kst(0) + k_lane, oA, pA, sA, qA, sB, mB, lB, pB, F_{}, T_{}, F_{});
+    sm_pre(sA, mA, lA, oA, 0);
+    slot(nullptr, kst(0) + k_lane, oB, pB, sB, qB, sA, mA, lA, pA, F_{}, T_{}, T_{});
+    copies_and_wait(0, 0);
+    // steps 1 .. n_iter-1: slots 2t and 2t+1 read V(t-1) (stage rv) and K(t) (stage r)
+    int r = 1, rv = 0, ktA = next_kt(0), ktB = 0;
+    for (int t = 1; t < n_iter; ++t) {
+      const char* vs = vst(rv) + v_lane;
+      const char* ks = kst(r) + k_lane;
+      sm_pre(sB, mB, lB, oB, ktB);  // S_B(t-1)
+      slot(vs, ks, oA, pA, sA, qA, sB, mB, lB, pB, T_{}, T_{}, T_{});
+      sm_pre(sA, mA, lA, oA, ktA);  // S_A(t)
+      slot(vs, ks, oB, pB, sB, qB, sA, mA, lA, pA, T_{}, T_{}, T_{});
+      copies_and_wait(t, r);
+      rv = r;
+      r = next_r(r);
+      ktA = next_kt(ktA);
+      ktB = next_kt(ktB);
+    }
+    // last step: P_A(n-1) with S_B(n-1); then P_B(n-1)
+    const char* vs = vst(rv) + v_lane;
+    sm_pre(sB, mB, lB, oB, ktB);
+    slot(vs, nullptr, oA, pA, sA, qA, sB, mB, lB, pB, T_{}, F_{}, T_{});
+    slot(vs, nullptr, oB, pB, sB, qB, sA, mA, lA, pA, T_{}, F_{}, F_{});
+  }
+
+  if (wave_on) {
+    auto store = [&](const f32x16 (&ov)[DB], const float (&l)[2], float m, int row, bool ok) {
+      const float lt = halves_sum(l[0] + l[1]);
+      const float inv = 1.0f / lt;
+      if (!ok) return;
+      __bf16* orow = static_cast<__bf16*>(p.o) + (((size_t)w.j * C + row) * H + w.h) * D;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          __bf16 v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(ov[d][4 * a + e] * inv);
+          uint2 raw;
+          __builtin_memcpy(&raw, v4, 8);
+          *reinterpret_cast<uint2*>(orow + 32 * d + 8 * a + 4 * hh) = raw;
+        }
+      if (p.lse && hh == 0)
+        p.lse[(size_t)w.h * p.n_inflight * C + (size_t)w.j * C + row] = (m + log2f(lt)) * kLn2;
+    };
+    store(oA, lA, mA, rowA, okA);
+    store(oB, lB, mB, rowB, okB);
+  }
+}
+
 // ---------------------------------------------------------------- fp32
-// Same schedule with fp32 operands on v_mfma_f32_32x32x2_f32 (two head_dim
-// or key values per instruction); weights stay fp32.
+// fp32 operands on v_mfma_f32_32x32x2_f32 (two head_dim or key values per
+// instruction), weights stay fp32. Plain schedule: copy tile t+1 while tile t
+// is consumed (two stages), QK, softmax, PV, barrier.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(wf::AttnParams p) {
   using G = Geo<float, D, NW>;
@@ -318,37 +765,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(wf::AttnParams p)
   char* smem = g_smem;
 
   const Work w = decode_block(blockIdx.x, p.n_inflight, p.n_heads, p.q_tiles);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = lane & 31, hh = lane >> 5;
-  const int C = p.chunk_tokens, H = p.n_heads, s_pad = p.s_pad;
+  const int C = p.chunk_tokens, H = p.n_heads;
   const int wrow = w.qt * (NW * 32) + wave * 32;
   const bool wave_on = wrow < C;
   const int row = wrow + qi;
   const bool row_ok = row < C;
   const size_t qoff = (((size_t)w.j * C + row) * H + w.h) * D;
 
+  const TileSrc src{static_cast<const char*>(p.k_pool), static_cast<const char*>(p.v_pool),
+                    (size_t)p.slot_elems * G::ES, (size_t)w.h * p.s_pad * D * G::ES, G::TILE, p.key_tiles,
+                    p.slots};
+  const int n_iter = (p.n_hist + w.j + 1) * p.key_tiles;
+  // two stages: stage b = K image at b*2*TILE, V image right after it
+  auto copy_kv = [&](int t) {
+    char* st = smem + (t & 1) * 2 * G::TILE;
+    copy_tile<G>(src.kpool + src.off(t), st, wave, lane);
+    copy_tile<G>(src.vpool + src.off(t), st + G::TILE, wave, lane);
+  };
+
+  copy_kv(0);
   f32x4 qop[QP];
   {
     const f32x4* qp = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.q) + qoff + hh * (D / 2));
 #pragma unroll
     for (int k = 0; k < QP; ++k) qop[k] = row_ok ? qp[k] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  TileSrc<G, D> src{static_cast<const char*>(p.k_pool), static_cast<const char*>(p.v_pool),
-                    (size_t)p.slot_elems * G::ES, (size_t)w.h * s_pad * D * G::ES,
-                    (size_t)w.h * D * s_pad * G::ES, p.slots};
-  const size_t v_row_bytes = (size_t)s_pad * G::ES;
-  const int ktc = p.key_tiles;
-  const int n_iter = (p.n_hist + w.j + 1) * ktc;
-
-  Stager<G> st;
-  {
-    const char *kb, *vb;
-    src.at(0, 0, kb, vb);
-    st.load(kb, vb, v_row_bytes, tid);
-    st.store(smem, tid);
-  }
-  __syncthreads();
+  wait_vm_barrier<0>();
 
   f32x16 o[DB];
 #pragma unroll
@@ -357,22 +802,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(wf::AttnParams p)
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
   float m_ref = -INFINITY, lsum = 0.f;
   const float sl2e = p.scale_log2e;
+  const int k_lane = key_of_arow(qi) * 16 + hh * QP * G::KPS;
+  const int v_lane = qi * 16;
 
-  int cl = 0, kt = 0;
   for (int it = 0; it < n_iter; ++it) {
-    const int valid = min(KT, C - kt * KT);
-    int ncl = cl, nkt = kt + 1;
-    if (nkt == ktc) {
-      nkt = 0;
-      ++ncl;
-    }
-    const bool more = it + 1 < n_iter;
-    if (more) {
-      const char *kb, *vb;
-      src.at(ncl, nkt, kb, vb);
-      st.load(kb, vb, v_row_bytes, tid);
-    }
-    const char* ks = smem + (it & 1) * G::STAGE;
+    if (it + 1 < n_iter) copy_kv(it + 1);
+    const char* ks = smem + (it & 1) * 2 * G::TILE + k_lane;
+    const char* vs = smem + (it & 1) * 2 * G::TILE + G::TILE + v_lane;
     if (wave_on) {
       f32x16 s[2];
 #pragma unroll
@@ -383,13 +819,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(wf::AttnParams p)
       for (int k = 0; k < QP; ++k) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          const int r = 32 * b + key_of_arow(qi);
-          const int c = hh * QP + k;
-          const f32x4 a = *reinterpret_cast<const f32x4*>(ks + r * (G::CK * 16) + ((c ^ swz_k(r)) << 4));
+          const f32x4 a = *reinterpret_cast<const f32x4*>(ks + k * G::KPS + b * 32 * 16);
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qop[k][e], s[b], 0, 0, 0);
         }
       }
+      const int kt = it % p.key_tiles;
+      const int valid = min(KT, C - kt * KT);
       if (valid < KT) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -402,7 +838,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(wf::AttnParams p)
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
-      mx = fmaxf(mx, xor32(mx));
+      mx = halves_max(mx);
       const float tmax = mx * sl2e;
       if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleLog2)) {
         const float mn = fmaxf(m_ref, tmax);
@@ -422,29 +858,26 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(wf::AttnParams p)
           s[b][e] = fast_exp2(fmaf(s[b][e], sl2e, nm));
           lsum += s[b][e];
         }
-      const char* vs = ks + G::K_BYTES;
+      // element r of block b is key 32b + 16(r/8) + 8hh + r%8; V piece
+      // 8b + 4(g/2) + 2hh + (g%2) (4 keys each) holds the keys of elements 4g..4g+3
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            const int r = 32 * d + qi;
-            const int c = 8 * b + 4 * (g >> 1) + 2 * hh + (g & 1);
-            const f32x4 a = *reinterpret_cast<const f32x4*>(vs + r * (G::CV * 16) + ((c ^ swz_v(r)) << 4));
+            const int c = 8 * b + 4 * (g >> 1) + (g & 1);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(vs + (c + 2 * hh) * G::VPS + d * 32 * 16);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], s[b][4 * g + e], o[d], 0, 0, 0);
           }
     }
-    if (more) st.store(smem + ((it + 1) & 1) * G::STAGE, tid);
-    __syncthreads();
-    cl = ncl;
-    kt = nkt;
+    wait_vm_barrier<0>();
   }
 
   if (wave_on) {
-    const float lt = lsum + xor32(lsum);
+    const float lt = halves_sum(lsum);
     const float inv = 1.0f / lt;
     if (row_ok) {
       float* orow = static_cast<float*>(p.o) + qoff;
@@ -478,19 +911,31 @@ namespace wf {
 hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& p, hipStream_t s) {
   const int C = kv.chunk_tokens;
   p.key_tiles = (C + KT - 1) / KT;
+#ifndef WF_ATTN_ONE_WAVE
+#define WF_ATTN_ONE_WAVE 0
+#endif
+  if (kv.dtype == WF_BF16 && WF_ATTN_ONE_WAVE) {
+    p.q_tiles = (C + 255) / 256;
+    const int grid = p.n_inflight * kv.n_heads * p.q_tiles;
+    if (kv.head_dim == 128)
+      return launch(attn_fwd_bf16_w1_kernel<128>, Geo<__bf16, 128, 4>::LDS, grid, 256, p, s);
+    return launch(attn_fwd_bf16_w1_kernel<64>, Geo<__bf16, 64, 4>::LDS, grid, 256, p, s);
+  }
   if (kv.dtype == WF_BF16) {
     constexpr int NW = 8;
     p.q_tiles = (C + NW * 32 - 1) / (NW * 32);
     const int grid = p.n_inflight * kv.n_heads * p.q_tiles;
     if (kv.head_dim == 128)
-      return launch(attn_fwd_bf16_kernel<128, NW>, Geo<__bf16, 128, NW>::LDS, grid, NW * 64, p, s);
-    return launch(attn_fwd_bf16_kernel<64, NW>, Geo<__bf16, 64, NW>::LDS, grid, NW * 64, p, s);
+      return launch(attn_fwd_bf16_kernel<128, NW, WF_ATTN_PINGPONG>, Geo<__bf16, 128, NW>::LDS, grid, NW * 64, p, s);
+    return launch(attn_fwd_bf16_kernel<64, NW, WF_ATTN_PINGPONG>, Geo<__bf16, 64, NW>::LDS, grid, NW * 64, p, s);
   }
   constexpr int NW = 4;
   p.q_tiles = (C + NW * 32 - 1) / (NW * 32);
   const int grid = p.n_inflight * kv.n_heads * p.q_tiles;
-  if (kv.head_dim == 128) return launch(attn_fwd_f32_kernel<128, NW>, Geo<float, 128, NW>::LDS, grid, NW * 64, p, s);
-  return launch(attn_fwd_f32_kernel<64, NW>, Geo<float, 64, NW>::LDS, grid, NW * 64, p, s);
+  // the fp32 kernel uses two stages of K + V
+  if (kv.head_dim == 128)
+    return launch(attn_fwd_f32_kernel<128, NW>, 4 * Geo<float, 128, NW>::TILE, grid, NW * 64, p, s);
+  return launch(attn_fwd_f32_kernel<64, NW>, 4 * Geo<float, 64, NW>::TILE, grid, NW * 64, p, s);
 }
 
 }  // namespace wf

@@ -2,8 +2,20 @@
 // K/V into a ring slot (append and cache refresh write the same way; the
 // cache-refresh stage is described in the Wave Forcing paper pages, Abstract).
 //
-// Slot layout (per pool, per slot):  K [H][S_pad][D]   V [H][D][S_pad]
-// Sources are token-major [C][H][D]. Both kernels are HBM-bound copies.
+// Slot layout. Each slot stores, per head, the chunk as a sequence of 64-key
+// tiles, and each tile as the exact image the attention kernel copies into
+// LDS, split into 16-byte pieces (E = elements per piece, 8 for bf16, 4 for fp32):
+//   K tile image: [D/E pieces][64 keys][16 B]   piece p of key k = K[k][p*E .. p*E+E)
+//   V tile image: [64/E pieces][D dims][16 B]   piece p of dim d = V[p*E .. p*E+E)[d]
+// so slot bytes = H * S_pad * D * sizeof(T) for each pool, tiles in key order.
+// A 64-key tile image is one contiguous block, which the attention kernel
+// moves with direct global->LDS loads; inside LDS this piece-major order lets
+// 16 lanes reading one piece of 16 different rows hit 16 different bank groups.
+// Keys past C inside the last tile are zero.
+//
+// One workgroup handles one (64-token tile, head): it stages the tile's K and
+// V rows in LDS (coalesced reads of the token-major source) and writes both
+// images with fully coalesced 16-byte stores. HBM-bound.
 #include "wf_internal.h"
 
 namespace {
@@ -16,70 +28,68 @@ __global__ void fill_zero_kernel(u32x4* p, size_t n16) {
     p[i] = z;
 }
 
-// K: every (token, head) row of D elements is one contiguous run on both sides.
-// One thread per 16-byte piece; consecutive threads read consecutive bytes.
-__global__ void k_rows_kernel(const u32x4* __restrict__ src, char* __restrict__ dst_slot, int C, int H,
-                              int row_bytes, int s_pad) {
-  const int per_row = row_bytes / 16;
-  const size_t total = (size_t)C * H * per_row;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const size_t row = i / per_row;  // = t*H + h
-    const int piece = (int)(i - row * per_row);
-    const int t = (int)(row / H), h = (int)(row - (size_t)t * H);
-    u32x4* d = reinterpret_cast<u32x4*>(dst_slot + ((size_t)h * s_pad + t) * row_bytes) + piece;
-    *d = src[i];
-  }
-}
-
-// V: transpose a [64 tokens][D] tile of one head into D rows of 64 tokens.
-// Tokens past C inside the last tile are written as zero (the padding).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void v_transpose_kernel(const T* __restrict__ src, T* __restrict__ dst_slot,
-                                                          int C, int H, int s_pad) {
-  constexpr int TT = 64;               // tokens per tile
-  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte piece
-  __shared__ T tile[TT][D + 2];        // +2 elements: column reads hit distinct banks
+__global__ __launch_bounds__(256) void kv_tile_kernel(const T* __restrict__ ksrc, const T* __restrict__ vsrc,
+                                                      char* __restrict__ kdst, char* __restrict__ vdst, int C, int H,
+                                                      int s_pad) {
+  constexpr int TT = 64;               // keys per tile
+  constexpr int E = 16 / sizeof(T);    // elements per 16-byte piece
+  constexpr int RB = D * sizeof(T);    // bytes per source row
+  constexpr int KROW = RB + 16;        // LDS row pitch of the K tile (16-byte aligned, conflict-free)
+  constexpr int VROW = D + 2;          // LDS row pitch (elements) of the V tile for column gathers
+  __shared__ __attribute__((aligned(16))) char kt[TT * KROW];
+  __shared__ T vt[TT][VROW];
   const int h = blockIdx.y;
-  const int t0 = blockIdx.x * TT;
-  // load: rows of D elements, 16 bytes per thread
-  constexpr int PIECES = TT * D / EPC;
+  const int tile = blockIdx.x;
+  const int t0 = tile * TT;
+
+  constexpr int PIECES = TT * D / E;  // 16-byte pieces per tile and tensor
   for (int i = threadIdx.x; i < PIECES; i += blockDim.x) {
-    const int r = i / (D / EPC), c = (i % (D / EPC)) * EPC;
+    const int r = i / (D / E), c = i % (D / E);
     const int t = t0 + r;
+    u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
     if (t < C) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + ((size_t)t * H + h) * D + c);
-      T vals[EPC];
-      __builtin_memcpy(vals, &raw, 16);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) tile[r][c + e] = vals[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) tile[r][c + e] = T(0);
+      const size_t off = ((size_t)t * H + h) * D + c * E;
+      kr = *reinterpret_cast<const u32x4*>(ksrc + off);
+      vr = *reinterpret_cast<const u32x4*>(vsrc + off);
     }
+    *reinterpret_cast<u32x4*>(kt + r * KROW + c * 16) = kr;
+    T vals[E];
+    __builtin_memcpy(vals, &vr, 16);
+#pragma unroll
+    for (int e = 0; e < E; ++e) vt[r][c * E + e] = vals[e];
   }
   __syncthreads();
-  // store: D rows, TT tokens each, 16 bytes per thread
-  constexpr int OUT_PIECES = D * TT / EPC;
-  for (int i = threadIdx.x; i < OUT_PIECES; i += blockDim.x) {
-    const int d = i / (TT / EPC), tc = (i % (TT / EPC)) * EPC;
-    T vals[EPC];
+
+  const size_t tile_off = (size_t)h * s_pad * RB + (size_t)tile * TT * RB;
+  u32x4* kimg = reinterpret_cast<u32x4*>(kdst + tile_off);
+  u32x4* vimg = reinterpret_cast<u32x4*>(vdst + tile_off);
+  for (int i = threadIdx.x; i < PIECES; i += blockDim.x) {
+    {  // K image position i = piece * 64 + key
+      const int p = i / TT, r = i % TT;
+      kimg[i] = *reinterpret_cast<const u32x4*>(kt + r * KROW + p * 16);
+    }
+    {  // V image position i = piece * D + dim
+      const int p = i / D, d = i % D;
+      T vals[E];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) vals[e] = tile[tc + e][d];
-    u32x4 raw;
-    __builtin_memcpy(&raw, vals, 16);
-    *reinterpret_cast<u32x4*>(dst_slot + ((size_t)h * D + d) * s_pad + t0 + tc) = raw;
+      for (int e = 0; e < E; ++e) vals[e] = vt[p * E + e][d];
+      u32x4 raw;
+      __builtin_memcpy(&raw, vals, 16);
+      vimg[i] = raw;
+    }
   }
 }
 
 template <typename T>
-hipError_t launch_v(const wf_kv_cache& kv, const void* v, void* vdst, hipStream_t s) {
+hipError_t launch_tiles(const wf_kv_cache& kv, const void* k, const void* v, char* kdst, char* vdst, hipStream_t s) {
   dim3 grid((kv.chunk_tokens + 63) / 64, kv.n_heads);
+  const T* kp = static_cast<const T*>(k);
+  const T* vp = static_cast<const T*>(v);
   if (kv.head_dim == 128)
-    v_transpose_kernel<T, 128><<<grid, 256, 0, s>>>(static_cast<const T*>(v), static_cast<T*>(vdst),
-                                                    kv.chunk_tokens, kv.n_heads, kv.s_pad);
+    kv_tile_kernel<T, 128><<<grid, 256, 0, s>>>(kp, vp, kdst, vdst, kv.chunk_tokens, kv.n_heads, kv.s_pad);
   else
-    v_transpose_kernel<T, 64><<<grid, 256, 0, s>>>(static_cast<const T*>(v), static_cast<T*>(vdst),
-                                                   kv.chunk_tokens, kv.n_heads, kv.s_pad);
+    kv_tile_kernel<T, 64><<<grid, 256, 0, s>>>(kp, vp, kdst, vdst, kv.chunk_tokens, kv.n_heads, kv.s_pad);
   return hipGetLastError();
 }
 
@@ -99,15 +109,8 @@ hipError_t launch_kv_write(const wf_kv_cache& kv, int slot, const void* k, const
   const size_t slot_bytes = kv.slot_elems * kv.esize;
   char* kdst = static_cast<char*>(kv.k_pool) + (size_t)slot * slot_bytes;
   char* vdst = static_cast<char*>(kv.v_pool) + (size_t)slot * slot_bytes;
-  const int row_bytes = kv.head_dim * (int)kv.esize;
-  const size_t pieces = (size_t)kv.chunk_tokens * kv.n_heads * row_bytes / 16;
-  const unsigned blocks = (unsigned)std::min<size_t>((pieces + 255) / 256, 16384);
-  k_rows_kernel<<<blocks, 256, 0, s>>>(static_cast<const u32x4*>(k), kdst, kv.chunk_tokens, kv.n_heads,
-                                       row_bytes, kv.s_pad);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (kv.dtype == WF_BF16) return launch_v<__bf16>(kv, v, vdst, s);
-  return launch_v<float>(kv, v, vdst, s);
+  if (kv.dtype == WF_BF16) return launch_tiles<__bf16>(kv, k, v, kdst, vdst, s);
+  return launch_tiles<float>(kv, k, v, kdst, vdst, s);
 }
 
 }  // namespace wf
