@@ -46,16 +46,14 @@ def visible_key_count(j: int, n_hist: int, chunk_tokens: int) -> int:
     return (n_hist + j + 1) * chunk_tokens
 
 
-def _head_chunk_task(q, k_vis, v_vis, h, rows, L, scale):
-    """Attention of the given query rows of one chunk, head h, over the first L keys."""
-    qh = np.asarray(q[rows, h, :], dtype=np.float64)
-    kh = np.asarray(k_vis[:L, h, :], dtype=np.float64)
-    vh = np.asarray(v_vis[:L, h, :], dtype=np.float64)
-    s = (qh @ kh.T) * scale
+def _head_chunk_task(qh, kh, vh, L, scale):
+    """Attention of query rows qh [R][D] of one chunk and head over the first L
+    keys of that head's keys kh and values vh ([keys][D], float64)."""
+    s = (qh @ kh[:L].T) * scale
     m = s.max(axis=1, keepdims=True)
     p = np.exp(s - m)
     l = p.sum(axis=1, keepdims=True)
-    o = (p @ vh) / l
+    o = (p @ vh[:L]) / l
     lse = m[:, 0] + np.log(l[:, 0])
     return o, lse
 
@@ -89,9 +87,23 @@ def chunk_causal_attention(
     out = np.empty((len(rows), H, D), dtype=np.float64)
     lse = np.empty((H, len(rows)), dtype=np.float64)
 
+    L_max = (n_hist + N) * C
+    heads = list(range(H))
+
+    def pool_map(fn, items):
+        if workers <= 1:
+            return [fn(x) for x in items]
+        from threadpoolctl import threadpool_limits  # one BLAS thread per task
+        with threadpool_limits(1), ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, items))
+
+    # each head's visible keys and values in float64, made once and shared by its tasks
+    kv64 = pool_map(lambda h: (np.asarray(k_vis[:L_max, h, :], dtype=np.float64),
+                               np.asarray(v_vis[:L_max, h, :], dtype=np.float64)), heads)
+
     tasks = []
     chunk_of_row = rows // C
-    for h in range(H):
+    for h in heads:
         for j in range(N):
             pos = np.nonzero(chunk_of_row == j)[0]
             L = visible_key_count(j, n_hist, C)
@@ -101,16 +113,12 @@ def chunk_causal_attention(
 
     def run(t):
         h, sel, r, L = t
-        o, ls = _head_chunk_task(q, k_vis, v_vis, h, r, L, scale)
+        qh = np.asarray(q[r, h, :], dtype=np.float64)
+        o, ls = _head_chunk_task(qh, kv64[h][0], kv64[h][1], L, scale)
         out[sel, h, :] = o
         lse[h, sel] = ls
 
-    if workers <= 1:
-        for t in tasks:
-            run(t)
-    else:
-        with ThreadPoolExecutor(max_workers=workers) as ex:
-            list(ex.map(run, tasks))
+    pool_map(run, tasks)
     return out, lse
 
 

@@ -41,14 +41,25 @@ def token_positions(n_tokens: int, first_global_chunk: int, chunk_tokens: int,
 
 def rope3d(x: np.ndarray, first_global_chunk: int, chunk_tokens: int,
            frames_per_chunk: int, grid_h: int, grid_w: int,
-           split: Sequence[int] = (44, 42, 42), theta: float = 10000.0) -> np.ndarray:
-    """Rotate x [n_tokens][H][D] (whole chunks) and return a float64 copy."""
+           split: Sequence[int] = (44, 42, 42), theta: float = 10000.0,
+           tokens=None) -> np.ndarray:
+    """Rotate x [n_tokens][H][D] (whole chunks) and return a float64 copy.
+    With ``tokens`` (indices into the block of whole chunks), x holds only
+    those tokens' rows, in that order."""
     n, H, D = x.shape
     d_t, d_h, d_w = split
     if d_t + d_h + d_w != D or d_t % 2 or d_h % 2 or d_w % 2:
         raise ValueError("axis split must be even and sum to head_dim")
-    pos = token_positions(n, first_global_chunk, chunk_tokens, frames_per_chunk,
-                          grid_h, grid_w).astype(np.float64)
+    if tokens is None:
+        pos = token_positions(n, first_global_chunk, chunk_tokens, frames_per_chunk,
+                              grid_h, grid_w).astype(np.float64)
+    else:
+        tokens = np.asarray(tokens)
+        if len(tokens) != n:
+            raise ValueError("one token index per row")
+        every = token_positions(int(tokens.max()) // chunk_tokens * chunk_tokens + chunk_tokens,
+                                first_global_chunk, chunk_tokens, frames_per_chunk, grid_h, grid_w)
+        pos = every[tokens].astype(np.float64)
     y = np.array(x, dtype=np.float64, copy=True)
     offset = 0
     for axis, d_a in enumerate((d_t, d_h, d_w)):

@@ -1,0 +1,211 @@
+"""The C ABI on the host, without a GPU: the library loads, exports exactly the
+functions include/wf.h declares, and every argument check returns its status
+code before any device work (a failed call leaves the cache table unchanged)."""
+import ctypes
+import os
+
+import pytest
+
+import chunk_causal_dit_amd as wf
+
+WF_OK, WF_E_NULL, WF_E_SHAPE, WF_E_DTYPE, WF_E_SLOT, WF_E_FULL, WF_E_EMPTY, WF_E_UNSUPPORTED, WF_E_HIP = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wf.library_path()):
+        from chunk_causal_dit_amd.build import build
+        build()
+    return wf.lib()
+
+
+class HostPools:
+    """256-byte aligned host addresses standing in for device pools (never dereferenced)."""
+
+    def __init__(self, nbytes=1 << 16):
+        self.buf = ctypes.create_string_buffer(nbytes + 512)
+        base = (ctypes.addressof(self.buf) + 255) // 256 * 256
+        self.k = ctypes.c_void_p(base)
+        self.v = ctypes.c_void_p(base + 256)
+
+
+def make_cache(L, n_slots=6, C=64, H=2, D=64, dtype=wf.WF_BF16):
+    pools = HostPools()
+    h = ctypes.c_void_p()
+    assert L.wf_kv_cache_create(ctypes.byref(h), pools.k, pools.v, n_slots, C, H, D, dtype, wf.WF_KV_ADOPT,
+                                None) == WF_OK
+    return h, pools
+
+
+def table(L, h):
+    arr = (ctypes.c_int * 64)()
+    n = ctypes.c_int()
+    assert L.wf_kv_get_table(h, arr, 64, ctypes.byref(n)) == WF_OK
+    return list(arr[: n.value])
+
+
+def set_table(L, h, slots):
+    arr = (ctypes.c_int * max(1, len(slots)))(*slots)
+    return L.wf_kv_set_table(h, arr, len(slots))
+
+
+def test_exports_match_header(L):
+    declared = wf.header_symbols()
+    exported = wf.exported_symbols()
+    assert declared == exported, (sorted(set(declared) - set(exported)), sorted(set(exported) - set(declared)))
+    assert len(declared) == 15
+
+
+def test_version_and_status_strings(L):
+    assert L.wf_version() == 100
+    for code in (WF_OK, WF_E_NULL, WF_E_SHAPE, WF_E_DTYPE, WF_E_SLOT, WF_E_FULL, WF_E_EMPTY, WF_E_UNSUPPORTED,
+                 WF_E_HIP):
+        assert L.wf_status_str(code).decode().startswith("WF_")
+    assert L.wf_status_str(-99) == b"unknown status"
+
+
+def test_pool_bytes(L):
+    # S_pad = chunk rounded up to 128 tokens; one pool = n_slots * H * S_pad * D * elem
+    assert L.wf_kv_pool_bytes(7, 4680, 12, 128, wf.WF_BF16) == 7 * 12 * 4736 * 128 * 2
+    assert L.wf_kv_pool_bytes(5, 64, 2, 64, wf.WF_F32) == 5 * 2 * 128 * 64 * 4
+    assert L.wf_kv_pool_bytes(5, 64, 2, 96, wf.WF_F32) == 0
+    assert b"head_dim" in L.wf_last_error()
+    assert L.wf_kv_pool_bytes(0, 64, 2, 64, wf.WF_F32) == 0
+    assert L.wf_kv_pool_bytes(65, 64, 2, 64, wf.WF_F32) == 0
+    assert L.wf_kv_pool_bytes(5, 0, 2, 64, wf.WF_F32) == 0
+    assert L.wf_kv_pool_bytes(5, 64, 2, 64, 7) == 0
+
+
+def test_create_argument_errors(L):
+    pools = HostPools()
+    h = ctypes.c_void_p()
+    args = lambda **kw: dict(dict(n=4, C=64, H=2, D=64, dt=wf.WF_BF16, fl=wf.WF_KV_ADOPT), **kw)
+
+    def create(k=pools.k, v=pools.v, **kw):
+        a = args(**kw)
+        return L.wf_kv_cache_create(ctypes.byref(h), k, v, a["n"], a["C"], a["H"], a["D"], a["dt"], a["fl"], None)
+
+    assert L.wf_kv_cache_create(None, pools.k, pools.v, 4, 64, 2, 64, 1, 0, None) == WF_E_NULL
+    assert create(k=None) == WF_E_NULL
+    assert create(D=80) == WF_E_UNSUPPORTED
+    assert create(dt=2) == WF_E_DTYPE
+    assert create(n=0) == WF_E_SHAPE
+    assert create(C=(1 << 20) + 1) == WF_E_SHAPE
+    assert create(H=0) == WF_E_SHAPE
+    assert create(fl=5) == WF_E_SHAPE
+    misaligned = ctypes.c_void_p(pools.k.value + 16)
+    assert create(k=misaligned) == WF_E_SHAPE
+    assert create() == WF_OK
+    assert L.wf_kv_cache_destroy(h) == WF_OK
+    assert L.wf_kv_cache_destroy(None) == WF_OK
+
+
+def test_table_operations(L):
+    h, pools = make_cache(L, n_slots=6)
+    assert table(L, h) == []
+    assert set_table(L, h, [4, 1, 3]) == WF_OK
+    assert table(L, h) == [4, 1, 3]
+    # invalid edits leave the table unchanged
+    assert set_table(L, h, [0, 0]) == WF_E_SLOT
+    assert set_table(L, h, [0, 6]) == WF_E_SLOT
+    assert set_table(L, h, [-1]) == WF_E_SLOT
+    assert set_table(L, h, list(range(7))) == WF_E_SHAPE
+    assert table(L, h) == [4, 1, 3]
+    assert L.wf_kv_evict(h, 4) == WF_E_EMPTY
+    assert L.wf_kv_evict(h, -1) == WF_E_SHAPE
+    assert table(L, h) == [4, 1, 3]
+    assert L.wf_kv_evict(h, 1) == WF_OK
+    assert table(L, h) == [1, 3]
+    assert L.wf_kv_evict(h, 0) == WF_OK
+    assert L.wf_kv_evict(None, 1) == WF_E_NULL
+    # get_table with a small buffer still reports the full length
+    arr = (ctypes.c_int * 1)()
+    n = ctypes.c_int()
+    assert L.wf_kv_get_table(h, arr, 1, ctypes.byref(n)) == WF_OK
+    assert n.value == 2 and arr[0] == 1
+    assert L.wf_kv_get_table(h, None, 0, ctypes.byref(n)) == WF_OK and n.value == 2
+    assert L.wf_kv_get_table(h, None, 1, ctypes.byref(n)) == WF_E_NULL
+    assert L.wf_kv_get_table(h, arr, 1, None) == WF_E_NULL
+    L.wf_kv_cache_destroy(h)
+
+
+def test_refresh_and_append_argument_errors(L):
+    h, pools = make_cache(L, n_slots=2)
+    k = ctypes.c_void_p(pools.k.value)
+    assert L.wf_kv_refresh(h, 0, k, k, None) == WF_E_SLOT  # empty table
+    assert L.wf_kv_append(h, None, k, None, None) == WF_E_NULL
+    assert L.wf_kv_append(h, ctypes.c_void_p(k.value + 4), k, None, None) == WF_E_SHAPE
+    assert set_table(L, h, [0, 1]) == WF_OK
+    assert L.wf_kv_append(h, k, k, None, None) == WF_E_FULL  # every slot in use
+    assert L.wf_kv_refresh(h, 2, k, k, None) == WF_E_SLOT
+    assert L.wf_kv_refresh(h, -1, k, k, None) == WF_E_SLOT
+    assert table(L, h) == [0, 1]
+    L.wf_kv_cache_destroy(h)
+
+
+def test_attention_argument_errors(L):
+    h, pools = make_cache(L, n_slots=4)
+    q = ctypes.c_void_p(pools.k.value)
+    lse = ctypes.cast(ctypes.c_void_p(pools.v.value), ctypes.POINTER(ctypes.c_float))
+    f = L.wf_chunk_causal_attn_fwd
+    assert f(None, h, 1, 0.1, q, None, None) == WF_E_NULL
+    assert f(q, None, 1, 0.1, q, None, None) == WF_E_NULL
+    assert f(q, h, 1, 0.1, None, None, None) == WF_E_NULL
+    assert f(q, h, 1, 0.1, q, None, None) == WF_E_EMPTY  # empty table
+    assert set_table(L, h, [2, 0, 1]) == WF_OK
+    assert f(q, h, 0, 0.1, q, None, None) == WF_E_SHAPE
+    assert f(q, h, 4, 0.1, q, None, None) == WF_E_EMPTY
+    assert f(q, h, 2, 0.0, q, None, None) == WF_E_SHAPE
+    assert f(q, h, 2, -0.1, q, None, None) == WF_E_SHAPE
+    assert f(q, h, 2, float("inf"), q, None, None) == WF_E_SHAPE
+    assert f(ctypes.c_void_p(q.value + 2), h, 2, 0.1, q, None, None) == WF_E_SHAPE
+    bad_lse = ctypes.cast(ctypes.c_void_p(pools.v.value + 2), ctypes.POINTER(ctypes.c_float))
+    assert f(q, h, 2, 0.1, q, bad_lse, None) == WF_E_SHAPE
+    # the int8 variant: needs bf16 and head_dim 128
+    ws = ctypes.c_void_p(pools.v.value)
+    g = L.wf_chunk_causal_attn_fwd_i8qk
+    assert g(q, h, 2, 0.1, None, q, lse, None) == WF_E_NULL
+    assert g(q, h, 2, 0.1, ws, q, lse, None) == WF_E_UNSUPPORTED  # head_dim 64
+    assert L.wf_attn_i8qk_workspace_bytes(h, 2) == 0
+    L.wf_kv_cache_destroy(h)
+    h32, p32 = make_cache(L, n_slots=4, D=128, dtype=wf.WF_F32)
+    assert g(q, h32, 2, 0.1, ws, q, lse, None) == WF_E_DTYPE
+    L.wf_kv_cache_destroy(h32)
+
+
+def test_rope_argument_errors(L):
+    pools = HostPools()
+    x = pools.k
+    r = L.wf_rope3d
+    assert r(None, 4, 1, 128, 1, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_NULL
+    assert r(x, 4, 1, 128, 1, 0, 1, 2, 2, 44, 42, 40, 1e4, None) == WF_E_SHAPE  # split sum
+    assert r(x, 4, 1, 128, 1, 0, 1, 2, 2, 43, 43, 42, 1e4, None) == WF_E_SHAPE  # odd split
+    assert r(x, 6, 1, 128, 1, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_SHAPE  # not whole chunks
+    assert r(x, 4, 1, 128, 1, 0, 1, 2, 2, 44, 42, 42, -1.0, None) == WF_E_SHAPE
+    assert r(x, 4, 1, 96, 1, 0, 1, 2, 2, 32, 32, 32, 1e4, None) == WF_E_UNSUPPORTED
+    assert r(x, 4, 1, 128, 5, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_DTYPE
+    assert r(x, 4, 1, 128, 1, -1, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_SHAPE
+    assert r(x, 0, 1, 128, 1, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_OK  # nothing to do
+
+
+def test_no_gpu_launch_fails_cleanly(L):
+    """Without a device a launch is refused: WF_E_HIP, and append leaves the table unchanged."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: launches would succeed")
+    h, pools = make_cache(L, n_slots=3)
+    k = ctypes.c_void_p(pools.k.value)
+    slot = ctypes.c_int(-1)
+    assert L.wf_kv_append(h, k, k, None, ctypes.byref(slot)) == WF_E_HIP
+    assert b"HIP" in L.wf_last_error()
+    assert table(L, h) == [] and slot.value == -1
+    L.wf_kv_cache_destroy(h)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    """No silent fallback: a missing library raises at first use."""
+    monkeypatch.setattr(wf, "_lib", None)
+    monkeypatch.setenv("WF_LIBRARY", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        wf.lib()

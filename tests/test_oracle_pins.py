@@ -369,23 +369,22 @@ def _attn_with_task(task):
     return attn
 
 
-def _task_no_scale(q, k, v, h, rows, L, scale):
-    return A.__dict__["_orig_task"](q, k, v, h, rows, L, 1.0)
+def _task_no_scale(qh, kh, vh, L, scale):
+    return A.__dict__["_orig_task"](qh, kh, vh, L, 1.0)
 
 
-def _task_wrong_head_v(q, k, v, h, rows, L, scale):
-    return A.__dict__["_orig_task"](q, k, np.roll(v, 1, axis=1), h, rows, L, scale)
+def _task_wrong_v_rows(qh, kh, vh, L, scale):
+    return A.__dict__["_orig_task"](qh, kh, np.roll(vh, 1, axis=0), L, scale)
 
 
-def _task_lse_without_max(q, k, v, h, rows, L, scale):
-    o, lse = A.__dict__["_orig_task"](q, k, v, h, rows, L, scale)
-    qh = q[rows, h].astype(np.float64)
-    s = qh @ k[:L, h].astype(np.float64).T * scale
+def _task_lse_without_max(qh, kh, vh, L, scale):
+    o, lse = A.__dict__["_orig_task"](qh, kh, vh, L, scale)
+    s = qh @ kh[:L].T * scale
     return o, lse - s.max(axis=1)
 
 
-def _task_keys_as_values(q, k, v, h, rows, L, scale):
-    return A.__dict__["_orig_task"](q, k, k, h, rows, L, scale)
+def _task_keys_as_values(qh, kh, vh, L, scale):
+    return A.__dict__["_orig_task"](qh, kh, kh, L, scale)
 
 
 A._orig_task = A._head_chunk_task
@@ -395,7 +394,7 @@ ATTN_MUTANTS = {
     "chunk_sees_next": _attn_with_visible(lambda j, Hs, C: (Hs + j + 2) * C),
     "history_ignored": _attn_with_visible(lambda j, Hs, C: (j + 1) * C),
     "no_scale": _attn_with_task(_task_no_scale),
-    "wrong_head_v": _attn_with_task(_task_wrong_head_v),
+    "wrong_value_rows": _attn_with_task(_task_wrong_v_rows),
     "lse_missing_max": _attn_with_task(_task_lse_without_max),
     "keys_as_values": _attn_with_task(_task_keys_as_values),
 }
@@ -480,3 +479,11 @@ def _quant_mutant(kind):
 def test_quant_mutants_are_caught(kind):
     with pytest.raises(AssertionError):
         check_int8_golden(_quant_mutant(kind))
+
+
+def test_rope_token_subset_equals_full():
+    x = _rand((2 * 60, 2, 12), 10)
+    full = R.rope3d(x, 3, 60, 3, 4, 5, split=(4, 4, 4))
+    idx = np.array([119, 0, 61, 7])
+    sub = R.rope3d(x[idx], 3, 60, 3, 4, 5, split=(4, 4, 4), tokens=idx)
+    np.testing.assert_array_equal(sub, full[idx])
