@@ -143,12 +143,24 @@ class KVCache:
                                         WF_KV_ZERO_FILL, _vp(_stream(stream))), "wf_kv_cache_create")
         self._h = h
 
-    # views of the pools in their documented layouts (for inspection and tests)
-    def k_slots(self) -> torch.Tensor:
-        return self.k_pool.view(self.dtype).view(self.n_slots, self.n_heads, self.s_pad, self.head_dim)
+    # decoded contents of one physical slot, [H][S_pad][D] (for inspection and tests)
+    def _slot_raw(self, pool: torch.Tensor, slot: int) -> torch.Tensor:
+        n = self.n_heads * self.s_pad * self.head_dim
+        return pool.view(self.dtype)[slot * n:(slot + 1) * n]
 
-    def v_slots(self) -> torch.Tensor:
-        return self.v_pool.view(self.dtype).view(self.n_slots, self.n_heads, self.head_dim, self.s_pad)
+    def k_slot(self, slot: int) -> torch.Tensor:
+        """K tile images [H][S_pad/64][D/E][64][E] (E = 16 bytes of elements) -> [H][S_pad][D]."""
+        H, S, D = self.n_heads, self.s_pad, self.head_dim
+        E = 16 // self.k_pool.view(self.dtype).element_size()
+        raw = self._slot_raw(self.k_pool, slot).view(H, S // 64, D // E, 64, E)
+        return raw.permute(0, 1, 3, 2, 4).reshape(H, S, D)
+
+    def v_slot(self, slot: int) -> torch.Tensor:
+        """V tile images [H][S_pad/64][64/E][D][E] -> [H][S_pad][D]."""
+        H, S, D = self.n_heads, self.s_pad, self.head_dim
+        E = 16 // self.v_pool.view(self.dtype).element_size()
+        raw = self._slot_raw(self.v_pool, slot).view(H, S // 64, 64 // E, D, E)
+        return raw.permute(0, 1, 2, 4, 3).reshape(H, S, D)
 
     @property
     def handle(self) -> _vp:

@@ -40,6 +40,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int KT = 64;  // keys per tile
@@ -97,6 +99,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // not sink the instructions producing these registers past this point (volatile
 // asm statements keep their order, and the barrier is one).
 __device__ __forceinline__ void pin_scores(f32x16& a, f32x16& b) { asm volatile("" : "+v"(a), "+v"(b)); }
+__device__ __forceinline__ void pin_scores(i32x16& a, i32x16& b) { asm volatile("" : "+v"(a), "+v"(b)); }
 __device__ __forceinline__ void pin_weights(bf16x8 (&p)[4]) {
   asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
 }
@@ -132,14 +135,20 @@ struct Geo {
   static_assert(CPW * NW == COPIES, "tile copies must split evenly over the waves");
 };
 
-// Direct HBM -> LDS copy of one tile image: wave w issues copies w, w+NW, ...
-template <typename G>
-__device__ __forceinline__ void copy_tile(const char* src, char* lds_dst, int wave, int lane) {
+// Direct HBM -> LDS copy of one image of BYTES bytes: wave w issues the 1 KB
+// copies w, w+NW, ...
+template <int BYTES, int NW>
+__device__ __forceinline__ void copy_image(const char* src, char* lds_dst, int wave, int lane) {
+  static_assert(BYTES % (1024 * NW) == 0, "image copies must split evenly over the waves");
 #pragma unroll
-  for (int i = 0; i < G::CPW; ++i) {
-    const int c = wave + i * (G::COPIES / G::CPW);
+  for (int i = 0; i < BYTES / (1024 * NW); ++i) {
+    const int c = wave + i * NW;
     __builtin_amdgcn_global_load_lds(src + c * 1024 + lane * 16, (LDS_AS void*)(lds_dst + c * 1024), 16, 0, 0);
   }
+}
+template <typename G>
+__device__ __forceinline__ void copy_tile(const char* src, char* lds_dst, int wave, int lane) {
+  copy_image<G::TILE, G::NT / 64>(src, lds_dst, wave, lane);
 }
 
 // Addresses of key tile t (logical chunk t / ktc, tile t % ktc) for head h.
@@ -182,12 +191,27 @@ extern __shared__ __attribute__((aligned(1024))) char g_smem[];
 #define WF_ATTN_LEAD_GROUP 1
 #endif
 
-template <int D, int NW, bool PINGPONG>
+// I8 = true: the int8-QK variant. S^T = K'^T Q^T runs on int8 MFMA over the
+// codes that attn_i8qk.hip wrote (K - mean and Q, 128-token blocks); the wave's
+// 32 query rows share one Q scale and a 64-key tile one K scale, so the
+// dequantization is one factor per (wave, tile) folded into the exp2 argument.
+// K code tiles come from the workspace in logical order, V from the cache.
+// P.V stays bf16.
+template <int D, bool I8>
+struct TileBytes {
+  static constexpr int K = KT * D * (I8 ? 1 : 2);
+  static constexpr int V = KT * D * 2;
+  static constexpr int LDS = 3 * K + 3 * V;
+};
+
+template <int D, int NW, bool PINGPONG, bool I8 = false>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p) {
   static_assert(NW == 8, "8 waves: two per SIMD");
   using G = Geo<__bf16, D, NW>;
-  constexpr int KS = D / 16;  // MFMA steps over head_dim (16 per step)
-  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  using TB = TileBytes<D, I8>;
+  constexpr int KS = D / 16;               // bf16 MFMA steps over head_dim (16 per step)
+  constexpr int KSQ = I8 ? D / 32 : KS;    // Q.K MFMA steps (int8: 32 per step)
+  constexpr int DB = D / 32;               // 32-row blocks of O^T
   char* smem = g_smem;
 
   const Work w = decode_block(blockIdx.x, p.n_inflight, p.n_heads, p.q_tiles);
@@ -205,41 +229,68 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
   const int ktc = p.key_tiles;
   const int n_vis = p.n_hist + w.j + 1;  // visible logical chunks
   const int n_iter = n_vis * ktc;
-  const char* kpool = static_cast<const char*>(p.k_pool);
+  const char* kpool = I8 ? reinterpret_cast<const char*>(p.k_codes) : static_cast<const char*>(p.k_pool);
   const char* vpool = static_cast<const char*>(p.v_pool);
   const size_t slot_bytes = (size_t)p.slot_elems * G::ES;
   const size_t head_off = (size_t)w.h * p.s_pad * D * G::ES;
+  // int8 K codes: [table position][head][s_pad / 64 tiles][TB::K bytes]
+  const size_t kchunk_bytes = (size_t)(p.s_pad / KT) * TB::K;
   // Wave-uniform cursor over the tiles in visiting order (chunk by chunk), so
-  // the loop needs no divisions: byte offset of the tile in a pool.
+  // the loop needs no divisions: byte offsets of the tile's K and V images.
   struct Cursor {
     int cl, kt;
-    size_t off;
+    size_t koff, voff;
+  };
+  auto chunk_start = [&](Cursor& c) {
+    c.voff = (size_t)p.slots[c.cl] * slot_bytes + head_off;
+    c.koff = I8 ? ((size_t)c.cl * H + w.h) * kchunk_bytes : c.voff;
   };
   auto cursor_at = [&](int t) {
     Cursor c;
     c.cl = t / ktc;
     c.kt = t - c.cl * ktc;
-    c.off = (size_t)p.slots[c.cl] * slot_bytes + head_off + (size_t)c.kt * G::TILE;
+    chunk_start(c);
+    c.voff += (size_t)c.kt * TB::V;
+    c.koff += (size_t)c.kt * TB::K;
     return c;
   };
   auto advance = [&](Cursor& c) {
-    c.off += G::TILE;
+    c.voff += TB::V;
+    c.koff += TB::K;
     if (++c.kt == ktc) {
       c.kt = 0;
-      if (++c.cl < n_vis) c.off = (size_t)p.slots[c.cl] * slot_bytes + head_off;
+      if (++c.cl < n_vis) chunk_start(c);
     }
   };
-  auto kst = [&](int r) { return smem + r * G::TILE; };                  // K stage r
-  auto vst = [&](int r) { return smem + (G::NSTAGE + r) * G::TILE; };   // V stage r
+  auto kst = [&](int r) { return smem + r * TB::K; };                   // K stage r
+  auto vst = [&](int r) { return smem + 3 * TB::K + r * TB::V; };      // V stage r
+  auto copy_k = [&](size_t off, char* dst) { copy_image<TB::K, NW>(kpool + off, dst, wave, lane); };
+  auto copy_v = [&](size_t off, char* dst) { copy_image<TB::V, NW>(vpool + off, dst, wave, lane); };
 
   // prologue copies: K(0) -> K stage 0, K(1) -> K stage 1, V(0) -> V stage 0
-  copy_tile<G>(kpool + cursor_at(0).off, kst(0), wave, lane);
-  if (n_iter > 1) copy_tile<G>(kpool + cursor_at(1).off, kst(1), wave, lane);
-  copy_tile<G>(vpool + cursor_at(0).off, vst(0), wave, lane);
+  copy_k(cursor_at(0).koff, kst(0));
+  if (n_iter > 1) copy_k(cursor_at(1).koff, kst(1));
+  copy_v(cursor_at(0).voff, vst(0));
 
-  // Stationary B operand: this lane's query row, half hh of head_dim.
-  bf16x8 qop[KS];
-  {
+  // Stationary B operand: this lane's query row, half hh of head_dim (bf16
+  // values, or int8 codes for I8).
+  bf16x8 qop[I8 ? 1 : KS];
+  i32x4 qop8[I8 ? KSQ : 1];
+  float sl2e = p.scale_log2e;
+  float* ksc = reinterpret_cast<float*>(smem + TB::LDS);  // I8: K scales of the visible chunks
+  if constexpr (I8) {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(p.q_codes + qoff + hh * (D / 2));
+#pragma unroll
+    for (int k = 0; k < KSQ; ++k) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (row_ok) raw = qp[k];
+      __builtin_memcpy(&qop8[k], &raw, 16);
+    }
+    const int nb = p.q_blocks;
+    if (wave_on) sl2e *= p.q_scales[((size_t)w.h * p.n_inflight + w.j) * nb + wrow / 128];
+    const float* ks_src = p.k_scales + (size_t)w.h * (p.n_hist + p.n_inflight) * nb;
+    for (int i = tid; i < n_vis * nb; i += NW * 64) ksc[i] = ks_src[i];
+  } else {
     const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) + qoff + hh * (D / 2));
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -250,7 +301,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
   }
   {  // V stage of "tile -1" (read once, multiplied by P = 0) must hold finite values
     u32x4* z = reinterpret_cast<u32x4*>(vst(G::NSTAGE - 1));
-    for (int i = tid; i < G::TILE / 16; i += G::NT) z[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < TB::V / 16; i += G::NT) z[i] = u32x4{0u, 0u, 0u, 0u};
   }
   wait_vm_barrier<0>();
 
@@ -260,6 +311,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
   f32x16 s[2];
+  i32x16 si[2];  // I8: integer scores
   bf16x8 pk[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
@@ -267,17 +319,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     for (int e = 0; e < 8; ++e) pk[kk][e] = (__bf16)0.f;
   float m_ref = -INFINITY;                  // reference max (log2 domain) of this lane's query row
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};     // this half's share of the row sum of weights
-  const float sl2e = p.scale_log2e;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   // per-lane operand offsets inside a stage; every op adds a compile-time constant
-  const int k_lane = key_of_arow(qi) * 16 + hh * KS * G::KPS;
+  const int k_lane = key_of_arow(qi) * 16 + hh * KSQ * G::KPS;
   const int v_lane = qi * 16 + hh * G::VPS;
 
   // MFMA block with an explicit operand pipeline: LDS reads run DEPTH
   // operands ahead of the MFMAs in one straight-line region. Op i < NPV is a
   // P.V step (kk = i / DB, d = i % DB); op i >= NPV a Q.K step (k, b).
   constexpr int DEPTH = WF_ATTN_LDS_DEPTH;
-  constexpr int NPV = 4 * DB, NQK = 2 * KS;
+  constexpr int NPV = 4 * DB, NQK = 2 * KSQ;
   auto mrun = [&](const char* vs, const char* ks, auto has_pv, auto has_qk) {
     constexpr bool PV = decltype(has_pv)::value, QK = decltype(has_qk)::value;
     constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NPV + NQK : NPV;
@@ -292,6 +343,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
       constexpr int i = decltype(ic)::value;
       if constexpr (i < NPV) {
         o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[i / DB], o[i % DB], 0, 0, 0);
+      } else if constexpr (I8) {
+        constexpr int j = i - NPV;
+        const i32x4 a8 = __builtin_bit_cast(i32x4, a);
+        if constexpr (j < 2)
+          si[j % 2] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a8, qop8[j / 2], i32x16{}, 0, 0, 0);
+        else
+          si[j % 2] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a8, qop8[j / 2], si[j % 2], 0, 0, 0);
       } else {
         constexpr int j = i - NPV;
         if constexpr (j < 2)
@@ -329,8 +387,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     if (WF_ATTN_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
   };
 
-  auto vblock = [&](int kt) {  // online softmax of a tile; kt = its index inside its chunk
+  // online softmax of a tile; kt = its index inside its chunk, cl its chunk
+  auto vblock = [&](int kt, int cl) {
     if (WF_ATTN_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
+    float ct = sl2e;  // log2-domain factor of the raw scores
+    if constexpr (I8) {
+      ct *= ksc[cl * p.q_blocks + (kt >> 1)];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[b][e] = (float)si[b][e];  // |score| < 2^24: exact
+    }
     const int valid = min(KT, C - kt * KT);
     if (valid < KT) {  // zero padding past the chunk end takes no weight
 #pragma unroll
@@ -348,7 +415,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
       for (int e = 2; e < 8; ++e) m4[c] = fmaxf(m4[c], s[c >> 1][(c & 1) * 8 + e]);
     }
     float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-    const float tmax = mx * sl2e;
+    const float tmax = mx * ct;
     if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleLog2)) {
       const float mn = fmaxf(m_ref, tmax);
       const float alpha = fast_exp2(m_ref - mn);
@@ -364,7 +431,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pk[2 * b + (e >> 3)][e & 7] = (__bf16)fast_exp2(fmaf(s[b][e], sl2e, nm));
+      for (int e = 0; e < 16; ++e) pk[2 * b + (e >> 3)][e & 7] = (__bf16)fast_exp2(fmaf(s[b][e], ct, nm));
     // row sum of the weights actually used (bf16-rounded), four accumulators
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -383,18 +450,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     const bool dk = t + 2 < n_iter, dv = t + 1 < n_iter;
     const int r1 = r == G::NSTAGE - 1 ? 0 : r + 1, r2 = r1 == G::NSTAGE - 1 ? 0 : r1 + 1;
     if (dk) {
-      copy_tile<G>(kpool + ck.off, kst(r2), wave, lane);
+      copy_k(ck.koff, kst(r2));
       advance(ck);
     }
     if (dv) {
-      copy_tile<G>(vpool + cv.off, vst(r1), wave, lane);
+      copy_v(cv.voff, vst(r1));
       advance(cv);
     }
-    constexpr int per = G::CPW;  // copy instructions per tensor and wave
+    constexpr int nk = TB::K / (1024 * NW), nv = TB::V / (1024 * NW);  // copy instructions per wave
     if (dk && dv)
-      wait_vm_barrier<2 * per>();
+      wait_vm_barrier<nk + nv>();
     else if (dv)
-      wait_vm_barrier<per>();
+      wait_vm_barrier<nv>();
     else
       wait_vm_barrier<0>();
   };
@@ -406,32 +473,38 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     }
   } else if (!PINGPONG || grp == 0) {
     // in-phase order (and ping-pong group 0): M_t, [barrier], V_t, copies + barrier
-    int vkt = 0;
+    int vkt = 0, vcl = 0;
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
       mblock(r);
       if (PINGPONG) {
-        pin_scores(s[0], s[1]);
+        if constexpr (I8)
+          pin_scores(si[0], si[1]);
+        else
+          pin_scores(s[0], s[1]);
         lds_barrier();
       }
       if (t < n_iter) {
-        vblock(vkt);
-        vkt = vkt + 1 == ktc ? 0 : vkt + 1;
+        vblock(vkt, vcl);
+        if (++vkt == ktc) vkt = 0, ++vcl;
       }
       pin_weights(pk);
       copies_and_wait(t, r);
     }
   } else {
     // ping-pong group 1, half a step behind: V_{t-1}, barrier, M_t, copies + barrier
-    int vkt = 0;
+    int vkt = 0, vcl = 0;
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
       if (t >= 1) {
-        vblock(vkt);
-        vkt = vkt + 1 == ktc ? 0 : vkt + 1;
+        vblock(vkt, vcl);
+        if (++vkt == ktc) vkt = 0, ++vcl;
       }
       pin_weights(pk);
       lds_barrier();
       mblock(r);
-      pin_scores(s[0], s[1]);
+      if constexpr (I8)
+        pin_scores(si[0], si[1]);
+      else
+        pin_scores(s[0], s[1]);
       copies_and_wait(t, r);
     }
   }
@@ -452,306 +525,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
           __builtin_memcpy(&raw, v4, 8);
           *reinterpret_cast<uint2*>(orow + 32 * d + 8 * a + 4 * hh) = raw;
         }
-      if (p.lse && hh == 0)
-        p.lse[(size_t)w.h * p.n_inflight * C + (size_t)w.j * C + row] = (m_ref + log2f(lt)) * kLn2;
+      if (p.lse && hh == 0) {
+        const size_t li = (size_t)w.h * p.n_inflight * C + (size_t)w.j * C + row;
+        float lse = (m_ref + log2f(lt)) * kLn2;
+        if constexpr (I8) lse += p.scale * p.qm[li];  // the keys' shared mean shift, added back
+        p.lse[li] = lse;
+      }
     }
   }
 }
 
-
-// ---------------------------------------------------------------- bf16, one wave per SIMD
-// Each wave owns 64 query rows as two halves A and B (32 rows each). Per half
-// the work on key tile t is Q_X(t) (MFMA: S = K Q^T), S_X(t) (softmax: S -> P)
-// and P_X(t) (MFMA: O += V^T P^T), strictly in that order. The two halves are
-// offset so that every slot pairs one half's MFMAs with the other half's
-// softmax:
-//   slot 2t+2:  MFMA { P_A(t), Q_A(t+1) }   VALU { S_B(t) }
-//   slot 2t+3:  MFMA { P_B(t), Q_B(t+1) }   VALU { S_A(t+1) }
-// Every register buffer is single (a half's S is overwritten only after its
-// softmax read it, its P only after its P.V read it). Inside a slot the
-// softmax's exp / bf16 / row-sum part is interleaved about three VALU per
-// MFMA; its row max, rescale test and rare rescale run just before the slot.
-// Slots 2t+2 and 2t+3 read V(t) and K(t+1); LDS copies and the one barrier per
-// step follow the three-stage schedule above.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_fwd_bf16_w1_kernel(wf::AttnParams p) {
-  constexpr int NW = 4;
-  using G = Geo<__bf16, D, NW>;
-  constexpr int KS = D / 16;  // MFMA steps over head_dim
-  constexpr int DB = D / 32;  // 32-row blocks of O^T
-  char* smem = g_smem;
-
-  const Work w = decode_block(blockIdx.x, p.n_inflight, p.n_heads, p.q_tiles);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qi = lane & 31, hh = lane >> 5;
-  const int C = p.chunk_tokens, H = p.n_heads;
-  const int wrow = w.qt * (NW * 64) + wave * 64;
-  const bool wave_on = wrow < C;
-  const int rowA = wrow + qi, rowB = wrow + 32 + qi;
-  const bool okA = rowA < C, okB = rowB < C;
-
-  const int ktc = p.key_tiles;
-  const int n_vis = p.n_hist + w.j + 1;
-  const int n_iter = n_vis * ktc;
-  const char* kpool = static_cast<const char*>(p.k_pool);
-  const char* vpool = static_cast<const char*>(p.v_pool);
-  const size_t slot_bytes = (size_t)p.slot_elems * G::ES;
-  const size_t head_off = (size_t)w.h * p.s_pad * D * G::ES;
-  struct Cursor {
-    int cl, kt;
-    size_t off;
-  };
-  auto cursor_at = [&](int t) {
-    Cursor c;
-    c.cl = t / ktc;
-    c.kt = t - c.cl * ktc;
-    c.off = (size_t)p.slots[c.cl] * slot_bytes + head_off + (size_t)c.kt * G::TILE;
-    return c;
-  };
-  auto advance = [&](Cursor& c) {
-    c.off += G::TILE;
-    if (++c.kt == ktc) {
-      c.kt = 0;
-      if (++c.cl < n_vis) c.off = (size_t)p.slots[c.cl] * slot_bytes + head_off;
-    }
-  };
-  auto kst = [&](int r) { return smem + r * G::TILE; };
-  auto vst = [&](int r) { return smem + (G::NSTAGE + r) * G::TILE; };
-
-  copy_tile<G>(kpool + cursor_at(0).off, kst(0), wave, lane);
-  if (n_iter > 1) copy_tile<G>(kpool + cursor_at(1).off, kst(1), wave, lane);
-  copy_tile<G>(vpool + cursor_at(0).off, vst(0), wave, lane);
-
-  bf16x8 qA[KS], qB[KS];
-  {
-    const size_t qoffA = (((size_t)w.j * C + rowA) * H + w.h) * D + hh * (D / 2);
-    const size_t qoffB = (((size_t)w.j * C + rowB) * H + w.h) * D + hh * (D / 2);
-    const u32x4* pa = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) + qoffA);
-    const u32x4* pb = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) + qoffB);
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      u32x4 ra = {0u, 0u, 0u, 0u}, rb = {0u, 0u, 0u, 0u};
-      if (okA) ra = pa[k];
-      if (okB) rb = pb[k];
-      __builtin_memcpy(&qA[k], &ra, 16);
-      __builtin_memcpy(&qB[k], &rb, 16);
-    }
-  }
-  wait_vm_barrier<0>();
-
-  f32x16 oA[DB], oB[DB], sA[2], sB[2];
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oA[d][e] = oB[d][e] = 0.f;
-  // Register classes: the stationary Q operands and the O accumulators live in
-  // AGPRs (MFMA reads B and C from there), leaving the VGPRs to S, P and the
-  // softmax.
-#pragma unroll
-  for (int k = 0; k < KS; ++k) asm volatile("" : "+a"(qA[k]), "+a"(qB[k]));
-#pragma unroll
-  for (int d = 0; d < DB; ++d) asm volatile("" : "+a"(oA[d]), "+a"(oB[d]));
-  bf16x8 pA[4], pB[4];
-  float mA = -INFINITY, mB = -INFINITY;
-  float lA[2] = {0.f, 0.f}, lB[2] = {0.f, 0.f};
-  const float sl2e = p.scale_log2e;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  const int k_lane = key_of_arow(qi) * 16 + hh * KS * G::KPS;
-  const int v_lane = qi * 16 + hh * G::VPS;
-  constexpr int DEPTH = 4;
-
-  // softmax part 1 (before the slot): padding mask, row max, rare rescale
-  auto sm_pre = [&](f32x16 (&sv)[2], float& m, float (&l)[2], f32x16 (&ov)[DB], int kt) {
-    const int valid = min(KT, C - kt * KT);
-    if (valid < KT) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (32 * b + key_of_elem(hh, e) >= valid) sv[b][e] = -INFINITY;
-    }
-    float m4[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      m4[c] = fmaxf(sv[c >> 1][(c & 1) * 8], sv[c >> 1][(c & 1) * 8 + 1]);
-#pragma unroll
-      for (int e = 2; e < 8; ++e) m4[c] = fmaxf(m4[c], sv[c >> 1][(c & 1) * 8 + e]);
-    }
-    const float tmax = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * sl2e;
-    if (__builtin_amdgcn_ballot_w64(tmax > m + kRescaleLog2)) {
-      const float mn = fmaxf(m, tmax);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      l[0] *= alpha;
-      l[1] *= alpha;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ov[d][e] *= alpha;
-        asm volatile("" : "+a"(ov[d]));  // back to the accumulator registers inside the branch
-      }
-    }
-  };
-  // A slot: the MFMAs of half X (P.V of tile t if PV, then Q.K of tile t+1
-  // if QK) interleaved unit by unit with the exp part of the softmax of half Y
-  // (if SM). Unit i = { LDS read for op i+DEPTH, MFMA op i, softmax element i:
-  // p = exp2(s*scale*log2e - m); every odd element also packs the pair to bf16
-  // and adds it to the row sum }. The sched_group_barrier sequence at the end
-  // pins exactly this order. Op i < NPV: P.V step (kk = i / DB, d = i % DB);
-  // otherwise Q.K step (k, b).
-  constexpr int NPV = 4 * DB, NQK = 2 * KS;
-  auto slot = [&](const char* vs, const char* ks, f32x16 (&ov)[DB], const bf16x8 (&pv)[4], f32x16 (&sv)[2],
-                  const bf16x8 (&qv)[KS], const f32x16 (&sy)[2], float my, float (&ly)[2], bf16x8 (&py)[4],
-                  auto has_pv, auto has_qk, auto has_sm) {
-    constexpr bool PV = decltype(has_pv)::value, QK = decltype(has_qk)::value, SM = decltype(has_sm)::value;
-    constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NPV + NQK : NPV, NM = I1 - I0;
-    constexpr int NU = SM ? (NM > 32 ? NM : 32) : NM;  // units: MFMAs and softmax elements
-    auto rd = [&](auto ic) -> bf16x8 {
-      constexpr int i = decltype(ic)::value;
-      if constexpr (i < NPV)
-        return *reinterpret_cast<const bf16x8*>(vs + (i / DB) * 2 * G::VPS + (i % DB) * 32 * 16);
-      else
-        return *reinterpret_cast<const bf16x8*>(ks + ((i - NPV) / 2) * G::KPS + ((i - NPV) % 2) * 32 * 16);
-    };
-    auto mm = [&](auto ic, const bf16x8& a) {
-      constexpr int i = decltype(ic)::value;
-      if constexpr (i < NPV) {
-        ov[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[i / DB], ov[i % DB], 0, 0, 0);
-      } else {
-        constexpr int j = i - NPV;
-        if constexpr (j < 2)
-          sv[j % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[j / 2], f32x16{}, 0, 0, 0);
-        else
-          sv[j % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[j / 2], sv[j % 2], 0, 0, 0);
-      }
-    };
-    const float nm = -my;
-    float pprev = 0.f;
-    bf16x8 buf[DEPTH];
-    static_for<0, DEPTH>([&](auto q) {
-      constexpr int i = I0 + decltype(q)::value;
-      if constexpr (i < I1) buf[decltype(q)::value] = rd(std::integral_constant<int, i>{});
-    });
-    static_for<0, NU>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      if constexpr (u < NM) {
-        constexpr int i = I0 + u;
-        const bf16x8 a = buf[u % DEPTH];
-        if constexpr (i + DEPTH < I1) buf[u % DEPTH] = rd(std::integral_constant<int, i + DEPTH>{});
-        mm(std::integral_constant<int, i>{}, a);
-      }
-      if constexpr (SM && u < 32) {
-        constexpr int b = u / 16, e = u % 16;
-        const float pe = fast_exp2(fmaf(sy[b][e], sl2e, nm));
-        if constexpr (u & 1) {
-          const bf16x2 pr = {(__bf16)pprev, (__bf16)pe};
-          py[2 * b + (e >> 3)][(e & 7) - 1] = pr[0];
-          py[2 * b + (e >> 3)][e & 7] = pr[1];
-          ly[(u >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ly[(u >> 1) & 1], false);
-        } else {
-          pprev = pe;
-        }
-      }
-    });
-    // results stay inside the slot (no sinking into the next block); S in VGPRs
-    if constexpr (QK) pin_scores(sv[0], sv[1]);
-    if constexpr (SM) {
-      pin_weights(py);
-      asm volatile("" : "+v"(ly[0]), "+v"(ly[1]));
-    }
-    // pin the unit order
-    __builtin_amdgcn_sched_group_barrier(0x100, DEPTH < NM ? DEPTH : NM, 0);
-    static_for<0, NU>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      if constexpr (u < NM) {
-        if constexpr (u + DEPTH < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      if constexpr (SM && u < 32) __builtin_amdgcn_sched_group_barrier(0x002, (u & 1) ? 4 : 2, 0);
-    });
-  };
-
-  Cursor ck = cursor_at(n_iter > 2 ? 2 : 0), cv = cursor_at(n_iter > 1 ? 1 : 0);
-  auto copies_and_wait = [&](int t, int r) {
-    const bool dk = t + 2 < n_iter, dv = t + 1 < n_iter;
-    const int r1 = r == G::NSTAGE - 1 ? 0 : r + 1, r2 = r1 == G::NSTAGE - 1 ? 0 : r1 + 1;
-    if (dk) {
-      copy_tile<G>(kpool + ck.off, kst(r2), wave, lane);
-      advance(ck);
-    }
-    if (dv) {
-      copy_tile<G>(vpool + cv.off, vst(r1), wave, lane);
-      advance(cv);
-    }
-    constexpr int per = G::CPW;
-    if (dk && dv)
-      wait_vm_barrier<2 * per>();
-    else if (dv)
-      wait_vm_barrier<per>();
-    else
-      wait_vm_barrier<0>();
-  };
-  auto next_r = [](int r) { return r == G::NSTAGE - 1 ? 0 : r + 1; };
-  auto next_kt = [&](int kt) { return kt + 1 == ktc ? 0 : kt + 1; };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-
-  if (!wave_on) {
-    for (int t = 0, r = 0; t < n_iter; ++t, r = next_r(r)) copies_and_wait(t, r);
-  } else {
-    // step 0: slot 0 = Q_A(0); slot 1 = Q_B(0) with S_A(0)
-    slot(nullptr, kst(0) + k_lane, oA, pA, sA, qA, sB, mB, lB, pB, F_{}, T_{}, F_{});
-    sm_pre(sA, mA, lA, oA, 0);
-    slot(nullptr, kst(0) + k_lane, oB, pB, sB, qB, sA, mA, lA, pA, F_{}, T_{}, T_{});
-    copies_and_wait(0, 0);
-    // steps 1 .. n_iter-1: slots 2t and 2t+1 read V(t-1) (stage rv) and K(t) (stage r)
-    int r = 1, rv = 0, ktA = next_kt(0), ktB = 0;
-    for (int t = 1; t < n_iter; ++t) {
-      const char* vs = vst(rv) + v_lane;
-      const char* ks = kst(r) + k_lane;
-      sm_pre(sB, mB, lB, oB, ktB);  // S_B(t-1)
-      slot(vs, ks, oA, pA, sA, qA, sB, mB, lB, pB, T_{}, T_{}, T_{});
-      sm_pre(sA, mA, lA, oA, ktA);  // S_A(t)
-      slot(vs, ks, oB, pB, sB, qB, sA, mA, lA, pA, T_{}, T_{}, T_{});
-      copies_and_wait(t, r);
-      rv = r;
-      r = next_r(r);
-      ktA = next_kt(ktA);
-      ktB = next_kt(ktB);
-    }
-    // last step: P_A(n-1) with S_B(n-1); then P_B(n-1)
-    const char* vs = vst(rv) + v_lane;
-    sm_pre(sB, mB, lB, oB, ktB);
-    slot(vs, nullptr, oA, pA, sA, qA, sB, mB, lB, pB, T_{}, F_{}, T_{});
-    slot(vs, nullptr, oB, pB, sB, qB, sA, mA, lA, pA, T_{}, F_{}, F_{});
-  }
-
-  if (wave_on) {
-    auto store = [&](const f32x16 (&ov)[DB], const float (&l)[2], float m, int row, bool ok) {
-      const float lt = halves_sum(l[0] + l[1]);
-      const float inv = 1.0f / lt;
-      if (!ok) return;
-      __bf16* orow = static_cast<__bf16*>(p.o) + (((size_t)w.j * C + row) * H + w.h) * D;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          __bf16 v4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(ov[d][4 * a + e] * inv);
-          uint2 raw;
-          __builtin_memcpy(&raw, v4, 8);
-          *reinterpret_cast<uint2*>(orow + 32 * d + 8 * a + 4 * hh) = raw;
-        }
-      if (p.lse && hh == 0)
-        p.lse[(size_t)w.h * p.n_inflight * C + (size_t)w.j * C + row] = (m + log2f(lt)) * kLn2;
-    };
-    store(oA, lA, mA, rowA, okA);
-    store(oB, lB, mB, rowB, okB);
-  }
-}
 
 // ---------------------------------------------------------------- fp32
 // fp32 operands on v_mfma_f32_32x32x2_f32 (two head_dim or key values per
@@ -911,23 +694,13 @@ namespace wf {
 hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& p, hipStream_t s) {
   const int C = kv.chunk_tokens;
   p.key_tiles = (C + KT - 1) / KT;
-#ifndef WF_ATTN_ONE_WAVE
-#define WF_ATTN_ONE_WAVE 0
-#endif
-  if (kv.dtype == WF_BF16 && WF_ATTN_ONE_WAVE) {
-    p.q_tiles = (C + 255) / 256;
-    const int grid = p.n_inflight * kv.n_heads * p.q_tiles;
-    if (kv.head_dim == 128)
-      return launch(attn_fwd_bf16_w1_kernel<128>, Geo<__bf16, 128, 4>::LDS, grid, 256, p, s);
-    return launch(attn_fwd_bf16_w1_kernel<64>, Geo<__bf16, 64, 4>::LDS, grid, 256, p, s);
-  }
   if (kv.dtype == WF_BF16) {
     constexpr int NW = 8;
     p.q_tiles = (C + NW * 32 - 1) / (NW * 32);
     const int grid = p.n_inflight * kv.n_heads * p.q_tiles;
     if (kv.head_dim == 128)
-      return launch(attn_fwd_bf16_kernel<128, NW, WF_ATTN_PINGPONG>, Geo<__bf16, 128, NW>::LDS, grid, NW * 64, p, s);
-    return launch(attn_fwd_bf16_kernel<64, NW, WF_ATTN_PINGPONG>, Geo<__bf16, 64, NW>::LDS, grid, NW * 64, p, s);
+      return launch(attn_fwd_bf16_kernel<128, NW, WF_ATTN_PINGPONG>, TileBytes<128, false>::LDS, grid, NW * 64, p, s);
+    return launch(attn_fwd_bf16_kernel<64, NW, WF_ATTN_PINGPONG>, TileBytes<64, false>::LDS, grid, NW * 64, p, s);
   }
   constexpr int NW = 4;
   p.q_tiles = (C + NW * 32 - 1) / (NW * 32);
@@ -936,6 +709,22 @@ hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& p, hipStream_t s) 
   if (kv.head_dim == 128)
     return launch(attn_fwd_f32_kernel<128, NW>, 4 * Geo<float, 128, NW>::TILE, grid, NW * 64, p, s);
   return launch(attn_fwd_f32_kernel<64, NW>, 4 * Geo<float, 64, NW>::TILE, grid, NW * 64, p, s);
+}
+
+hipError_t launch_attn_fwd_i8qk(const wf_kv_cache& kv, AttnParams& p, void* workspace, hipStream_t s) {
+  if (kv.dtype != WF_BF16 || kv.head_dim != 128) return hipErrorInvalidValue;
+  const int n_tab = p.n_hist + p.n_inflight;
+  const int nb = (kv.chunk_tokens + 127) / 128;
+  // the K scales of every visible chunk sit in LDS after the tile stages
+  const int lds = TileBytes<128, true>::LDS + (n_tab * nb * 4 + 15) / 16 * 16;
+  if (n_tab * nb > 16384 || lds > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t e = launch_quant_i8(kv, p, workspace, s);
+  if (e != hipSuccess) return e;
+  constexpr int NW = 8;
+  p.key_tiles = (kv.chunk_tokens + KT - 1) / KT;
+  p.q_tiles = (kv.chunk_tokens + NW * 32 - 1) / (NW * 32);
+  const int grid = p.n_inflight * kv.n_heads * p.q_tiles;
+  return launch(attn_fwd_bf16_kernel<128, NW, WF_ATTN_PINGPONG, true>, lds, grid, NW * 64, p, s);
 }
 
 }  // namespace wf

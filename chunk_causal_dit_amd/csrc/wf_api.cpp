@@ -216,6 +216,7 @@ static int fill_attn_params(const void* q, const wf_kv_cache* kv, int n_inflight
   p.n_inflight = n_inflight;
   p.n_hist = (int)kv->table.size() - n_inflight;
   p.scale_log2e = scale * 1.4426950408889634f;
+  p.scale = scale;
   for (size_t i = 0; i < kv->table.size(); ++i) p.slots[i] = kv->table[i];
   return ok();
 }
@@ -241,10 +242,12 @@ WF_EXPORT int wf_chunk_causal_attn_fwd_i8qk(const void* q, const wf_kv_cache* kv
   if (kv && kv->dtype != WF_BF16) return fail(WF_E_DTYPE, "%s: needs a bf16 cache", who);
   if (kv && kv->head_dim != 128) return fail(WF_E_UNSUPPORTED, "%s: needs head_dim 128", who);
   if (!aligned(workspace, 256)) return fail(WF_E_SHAPE, "%s: workspace must be 256-byte aligned", who);
+  if (kv && kv->table.size() * (size_t)((kv->chunk_tokens + 127) / 128) > 16384)
+    return fail(WF_E_SHAPE, "%s: table length x 128-token blocks per chunk exceeds 16384", who);
   AttnParams p;
   int st = fill_attn_params(q, kv, n_inflight, scale, out, lse, p, who);
   if (st != WF_OK) return st;
-  return hip_status(launch_attn_fwd_i8qk(*kv, p, workspace, scale, static_cast<hipStream_t>(stream)), who);
+  return hip_status(launch_attn_fwd_i8qk(*kv, p, workspace, static_cast<hipStream_t>(stream)), who);
 }
 
 WF_EXPORT const char* wf_status_str(int status) {

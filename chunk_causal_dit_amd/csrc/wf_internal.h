@@ -69,6 +69,14 @@ struct AttnParams {
   int q_tiles;     // query tiles per chunk
   int key_tiles;   // key tiles per chunk
   float scale_log2e;
+  float scale;
+  // int8-QK path only (workspace arrays, see attn_i8qk.hip)
+  const signed char* q_codes;  // [N*C][H][D]
+  const float* q_scales;       // [H][N][q_blocks]
+  const signed char* k_codes;  // [n_tab][H][key_tiles][64*D] tile images, logical order
+  const float* k_scales;       // [H][n_tab][q_blocks]
+  const float* qm;             // [H][N*C]
+  int q_blocks;                // 128-token blocks per chunk
   int slots[WF_MAX_TABLE];  // physical slot of logical chunk c = 0..n_hist+n_inflight-1
 };
 
@@ -80,7 +88,8 @@ struct I8Layout {
   int blocks_per_chunk;
 };
 I8Layout i8_layout(const wf_kv_cache& kv, int n_inflight);
-hipError_t launch_attn_fwd_i8qk(const wf_kv_cache& kv, AttnParams& prm, void* workspace,
-                                float scale, hipStream_t s);
+// Quantizes K - mean and Q into the workspace and fills prm's int8 fields.
+hipError_t launch_quant_i8(const wf_kv_cache& kv, AttnParams& prm, void* workspace, hipStream_t s);
+hipError_t launch_attn_fwd_i8qk(const wf_kv_cache& kv, AttnParams& prm, void* workspace, hipStream_t s);
 
 }  // namespace wf

@@ -5,13 +5,13 @@
  * What a round is. Wave Forcing denoises several video chunks at staggered
  * noise levels at once and re-runs a finished chunk to refresh the history
  * cache, one output chunk per round (Wave Forcing paper pages, Abstract:
- * "1F1C: one output chunk per concurrent forward round"). The in-flight
+ * the 1F1C schedule finishes one chunk per concurrent forward). The in-flight
  * chunks of a round (refresh chunk first, then the denoising chunks from
  * cleanest to noisiest; README usage on the airadar.tv summaries: wp-size =
  * step count + 1) form one query block. A chunk attends to the cached
  * history, to every earlier (cleaner) in-flight chunk and to itself, never to
- * a later one (Abstract: "chunk-wise causal attention to access earlier,
- * cleaner chunks before their denoising is complete").
+ * a later one (Abstract: chunk-wise causal attention reads earlier, cleaner
+ * chunks while their denoising is still under way).
  *
  * Conventions shared by every call
  *  - Pointers named k, v, q, x, out, workspace, lse, k_pool, v_pool are DEVICE
@@ -67,9 +67,17 @@ typedef struct wf_kv_cache wf_kv_cache;
  *
  * Storage: two caller-owned device pools of n_slots chunk slots each.
  * A slot holds one chunk of chunk_tokens tokens for all heads, padded to
- * S_pad = chunk_tokens rounded up to a multiple of 128 tokens:
- *   K pool: [n_slots][n_heads][S_pad][head_dim]   (token rows)
- *   V pool: [n_slots][n_heads][head_dim][S_pad]   (transposed: key-contiguous)
+ * S_pad = chunk_tokens rounded up to a multiple of 128 tokens, as images of
+ * 64-key tiles that the attention kernel copies byte for byte into LDS.
+ * With E = 16 / sizeof(element) (8 for bf16, 4 for fp32):
+ *   K pool: [n_slots][n_heads][S_pad/64 tiles][head_dim/E][64 keys][E]
+ *           (16-byte pieces of head_dim, key-major inside a piece)
+ *   V pool: [n_slots][n_heads][S_pad/64 tiles][64/E][head_dim][E]
+ *           (16-byte runs of E consecutive keys, one run per head_dim row)
+ * Element (key t, dim d) of head h in slot s therefore sits at K index
+ *   ((s*n_heads + h)*S_pad/64 + t/64)*64*head_dim + (d/E)*64*E + (t%64)*E + d%E
+ * and V index
+ *   ((s*n_heads + h)*S_pad/64 + t/64)*64*head_dim + ((t%64)/E)*head_dim*E + d*E + t%E.
  * Padding is zero and stays zero. A host-side table lists the slots of the
  * cache's chunks in logical order, oldest first; at attention time the last
  * n_inflight entries are the in-flight chunks (refresh chunk first) and the
@@ -168,7 +176,17 @@ int wf_chunk_causal_attn_fwd(const void* q, const wf_kv_cache* kv, int n_infligh
  * The mean shift changes no softmax row; lse refers to the unshifted keys
  * (the kernel adds scale * <q^_i, mean_h>, q^ the dequantized query).
  * workspace: device memory of wf_attn_i8qk_workspace_bytes() bytes, 256-byte
- * aligned, caller-owned, overwritten by every call.
+ * aligned, caller-owned, overwritten by every call. After a call it holds,
+ * each array starting at the next multiple of 256 bytes, in this order
+ * (n_tab = table length, N = n_inflight, C = chunk_tokens, nb = ceil(C/128)):
+ *   f64 [n_tab][H][128]  per-chunk key sums        f32 [H][128] key mean
+ *   i8  [n_tab][H][S_pad/64][8][64][16]  K - mean codes as 64-key tile images
+ *       (16-dim pieces, key-major), in table order, zero past each chunk end
+ *   f32 [H][n_tab][nb] K block scales   i8 [N*C][H][128] Q codes
+ *   f32 [H][N][nb] Q block scales       f32 [H][N*C] <q^_i, mean_h>
+ * Limit: the K scales of all table entries (n_tab * nb floats) must fit in
+ * 64 KB of LDS beside the tile stages, i.e. n_tab * nb <= 16384; larger
+ * rounds return WF_E_SHAPE.
  * ------------------------------------------------------------------------ */
 size_t wf_attn_i8qk_workspace_bytes(const wf_kv_cache* kv, int n_inflight);
 

@@ -4,10 +4,10 @@ What is computed. Wave Forcing packs the in-flight chunks of one 1F1C round
 (the cache-refresh chunk, then the denoising chunks from cleanest to noisiest)
 into one query block. A chunk may read the history cache, every earlier (and
 therefore cleaner) in-flight chunk and itself, but no later chunk
-(Wave Forcing paper pages, Abstract: "chunk-wise causal attention to access
-earlier, cleaner chunks before their denoising is complete"; airadar.tv
-summaries, first paragraph: later chunks read the cleaner context of earlier
-chunks still being denoised).
+(Wave Forcing paper pages, Abstract: the chunk-wise causal attention lets a
+chunk read earlier, cleaner chunks whose denoising is not finished yet;
+airadar.tv summaries, first paragraph: later chunks read the cleaner context
+of earlier chunks still being denoised).
 
 Readings taken where the pages are silent:
   * inside a chunk attention is full (bidirectional): "chunk-wise" causality

@@ -2,8 +2,8 @@
 
 The pages describe a history cache that later chunks read and a cache-refresh
 stage that re-runs a finished chunk so that its clean K/V replaces the noisy
-one (Wave Forcing paper pages, Abstract: "serialized denoising and
-history-cache refresh require two forward passes"; WF runs the refresh stage
+one (Wave Forcing paper pages, Abstract: done one after the other, denoising
+and the cache refresh cost two forward passes; WF runs the refresh stage
 concurrently with the denoising stages). The model keeps the semantics only:
 an ordered list of chunk entries, oldest first; no slots, no padding.
 

@@ -71,11 +71,15 @@ def gpu_round(wf, inp, table=None, n_slots=None, with_lse=True):
     return out, lse, cache
 
 
+def oracle_workers() -> int:
+    return min(16, len(os.sched_getaffinity(0)))
+
+
 def oracle_round(inp, rows=None, workers=None):
     cfg = inp.cfg
     k = np.concatenate([inp.k_hist, inp.k_in])
     v = np.concatenate([inp.v_hist, inp.v_in])
-    workers = workers or min(16, len(os.sched_getaffinity(0)))
+    workers = workers or oracle_workers()
     return OA.chunk_causal_attention(inp.q, k, v, cfg.n_hist, cfg.chunk_tokens, cfg.scale, rows=rows,
                                      workers=workers)
 
