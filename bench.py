@@ -1,6 +1,6 @@
 """Benchmark of one Wave Forcing round's hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config wan13b_4step]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
 
 One step = one 1F1C round of one layer on synthetic inputs already resident
 in HBM: append the new noisiest chunk to the history cache, refresh the
@@ -13,8 +13,11 @@ oldest history chunk (host-only). The workload is the Wan2.1-1.3B-shaped
 Prints ONE JSON line. value = effective attention FLOPs per round / step time
 (TFLOP/s); effective FLOPs = 4 * head_dim per visible (query, key) pair and
 head (padding, skipped tiles and softmax not counted). Also reported: the
-attention kernel alone against the bf16 MFMA peak (roofline), chunk-rounds/s,
-and the fp64 oracle timed on the host on a bounded sample of the same round.
+attention kernel alone against the bf16 MFMA peak (roofline, timed with
+events on the stream it runs on), chunk-rounds/s, the cache writes against
+HBM bandwidth and, unless --no-extras, the long-rollout round with 3D RoPE
+and the 14B-shaped int8-QK round; and the fp64 oracle timed on the host on a
+bounded sample of the same round.
 """
 from __future__ import annotations
 
@@ -30,13 +33,19 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import CONFIGS, RoundConfig, make_round_inputs  # noqa: E402
+from workloads import CONFIGS, RoundConfig, make_rollout_init, make_rollout_round, make_round_inputs  # noqa: E402
 
-MI355X_BF16_DENSE_TFLOPS = 2500.0  # published dense bf16 MFMA peak
-MI355X_HBM_GBS = 8000.0
+# Published MI355X peaks.
+BF16_DENSE_TFLOPS = 2500.0
+INT8_DENSE_TOPS = 5000.0
+HBM_GBS = 8000.0
+# int8-QK round: half of the effective operations run at the int8 rate (Q.K), half at the bf16
+# rate (P.V), so the peak for the mix is 1 / (0.5 / 5000 + 0.5 / 2500) TOP/s.
+I8QK_MIXED_PEAK = 1.0 / (0.5 / INT8_DENSE_TOPS + 0.5 / BF16_DENSE_TFLOPS)
 METRIC = "effective attention TFLOP/s per 1F1C round (% bf16 MFMA peak); chunk-rounds/s"
 PROFILES = os.path.join(ROOT, "profiles")
 ATTN_SRC = os.path.join(ROOT, "chunk_causal_dit_amd", "csrc", "attn_fwd.hip")
+ATTN_KERNEL = "attn_fwd_bf16_kernel<128, 8, true, false>"
 
 
 def effective_pairs_per_head(cfg: RoundConfig) -> int:
@@ -49,10 +58,23 @@ def effective_flops(cfg: RoundConfig) -> float:
     return 4.0 * cfg.head_dim * cfg.n_heads * effective_pairs_per_head(cfg)
 
 
-def kv_write_bytes(cfg: RoundConfig) -> float:
-    """HBM bytes of the round's cache writes: n_inflight chunks of K and V, read once, written once."""
-    es = 2 if cfg.dtype == "bf16" else 4
-    return 2.0 * 2.0 * cfg.n_inflight * cfg.chunk_tokens * cfg.n_heads * cfg.head_dim * es
+def executed_flops(cfg: RoundConfig, q_rows: int = 256, key_tile: int = 64) -> float:
+    """FLOPs the kernel issues: whole query tiles of q_rows rows (the tail padded), whole key
+    tiles of every visible chunk (the tail tile padded)."""
+    C = cfg.chunk_tokens
+    qpad = -(-C // q_rows) * q_rows
+    kpad = -(-C // key_tile) * key_tile
+    return 4.0 * cfg.head_dim * cfg.n_heads * sum(qpad * (cfg.n_hist + j + 1) * kpad for j in range(cfg.n_inflight))
+
+
+def chunk_bytes(cfg: RoundConfig) -> float:
+    return float(cfg.chunk_tokens * cfg.n_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4))
+
+
+def attention_min_bytes(cfg: RoundConfig) -> float:
+    """Least HBM traffic of one attention launch: Q read and O written once, every visible
+    K and V chunk read once (LSE not counted)."""
+    return chunk_bytes(cfg) * (2 * cfg.n_inflight + 2 * (cfg.n_hist + cfg.n_inflight))
 
 
 def source_hash(path: str) -> str:
@@ -60,7 +82,7 @@ def source_hash(path: str) -> str:
 
 
 def load_traffic(cfg_name: str):
-    """HBM traffic per attention launch from the committed rocprofv3 --pmc summary, or None
+    """HBM bytes per attention launch from the committed rocprofv3 --pmc summary, or None
     when there is none or the kernel source changed since it was taken."""
     path = os.path.join(PROFILES, f"attn_fwd_{cfg_name}_pmc.json")
     if not os.path.exists(path):
@@ -71,11 +93,20 @@ def load_traffic(cfg_name: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def pct(a, q):
+    return float(np.percentile(a, q))
+
+
+def ms_summary(ms) -> dict:
+    ms = np.asarray(ms)
+    return {"ms_mean": float(ms.mean()), "ms_median": pct(ms, 50), "ms_p10": pct(ms, 10), "ms_p90": pct(ms, 90)}
+
+
 def cpu_baseline(cfg: RoundConfig, inp, rows_per_chunk: int):
     """The fp64 oracle on a bounded sample of the round (every head, the first
     rows_per_chunk query rows of every in-flight chunk), in effective TFLOP/s."""
     import oracle.attention as OA
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     cores = len(os.sched_getaffinity(0))
     C = cfg.chunk_tokens
@@ -83,6 +114,7 @@ def cpu_baseline(cfg: RoundConfig, inp, rows_per_chunk: int):
     rows = np.concatenate([j * C + np.arange(r) for j in range(cfg.n_inflight)])
     k = np.concatenate([inp.k_hist, inp.k_in])
     v = np.concatenate([inp.v_hist, inp.v_in])
+    blas = sorted({i.get("internal_api", "?") for i in threadpool_info() if i.get("user_api") == "blas"})
     with threadpool_limits(1):
         t0 = time.perf_counter()
         OA.chunk_causal_attention(inp.q, k, v, cfg.n_hist, C, cfg.scale, rows=rows, workers=cores)
@@ -95,10 +127,189 @@ def cpu_baseline(cfg: RoundConfig, inp, rows_per_chunk: int):
         "kind": "oracle",
         "sample": f"{r} query rows of each of the {cfg.n_inflight} in-flight chunks x {cfg.n_heads} heads "
                   f"({flops / effective_flops(cfg):.1%} of the round's effective FLOPs), numpy fp64, "
-                  f"thread pool over (head, chunk) tasks, BLAS 1 thread per task",
+                  f"thread pool over (head, chunk) tasks, BLAS ({','.join(blas) or '?'}) 1 thread per task",
         "seconds": dt,
         "round_seconds_extrapolated": dt * effective_flops(cfg) / flops,
+        "chunk_rounds_per_s": flops / dt / effective_flops(cfg),
     }
+
+
+class Timer:
+    """Events recorded on one stream; pairs give the GPU time between marks."""
+
+    def __init__(self, torch, stream, n_marks):
+        self.torch, self.stream = torch, stream
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_marks)]
+
+    def mark(self, i):
+        self.ev[i].record(self.stream)
+
+    def ms(self, a, b):
+        return self.ev[a].elapsed_time(self.ev[b])
+
+
+def dev_bf16(torch, a):
+    return torch.from_numpy(a).to("cuda").to(torch.bfloat16)
+
+
+def bench_round(torch, wf, cfg, steps, warmup, stream):
+    """The headline step; returns timings and the resident state."""
+    C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
+    inp = make_round_inputs(cfg)
+    q, k_in, v_in = (dev_bf16(torch, a) for a in (inp.q, inp.k_in, inp.v_in))
+    k_hist, v_hist = dev_bf16(torch, inp.k_hist), dev_bf16(torch, inp.v_hist)
+    kc = [k_in[j * C:(j + 1) * C] for j in range(N)]
+    vc = [v_in[j * C:(j + 1) * C] for j in range(N)]
+    # steady state between rounds: n_hist history chunks + the N-1 continuing in-flight chunks
+    cache = wf.KVCache(Hs + N, C, H, D, torch.bfloat16)
+    for c in range(Hs):
+        cache.append(k_hist[c * C:(c + 1) * C], v_hist[c * C:(c + 1) * C])
+    for j in range(N - 1):
+        cache.append(kc[j], vc[j])
+    out = torch.empty_like(q)
+    lse = torch.empty((H, N * C), dtype=torch.float32, device="cuda")
+
+    def step(t=None):
+        if t:
+            t.mark(0)
+        cache.append(kc[N - 1], vc[N - 1])              # new noisiest chunk
+        for j in range(N - 1):                          # this round's K/V of the continuing chunks
+            cache.refresh(Hs + j, kc[j], vc[j])
+        if t:
+            t.mark(1)
+        wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, lse=lse)
+        if t:
+            t.mark(2)
+        cache.evict(1)                                  # the refresh chunk is history from now on
+
+    for _ in range(warmup):
+        step()
+    timers = [Timer(torch, stream, 3) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(timers[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kv_ms = [t.ms(0, 1) for t in timers]
+    attn_ms = [t.ms(1, 2) for t in timers]
+    return inp, wall * 1e3 / steps, kv_ms, attn_ms
+
+
+def bench_rollout(torch, wf, cfg, rounds, warmup, stream):
+    """Long-rollout steady state: per round rope3d(Q), rope3d(K), append, refresh, attention,
+    evict, on a permuted 12-slot ring. Timing only (the values are those of round 0, rotated
+    again every round)."""
+    from workloads import slot_permutation
+    C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
+    fpc, gh, gw, split = cfg.frames_per_chunk, cfg.grid_h, cfg.grid_w, cfg.rope_split
+    k0, v0 = make_rollout_init(cfg)
+    kd, vd = dev_bf16(torch, k0), dev_bf16(torch, v0)
+    del k0, v0
+    n0 = Hs + N - 1
+    cache = wf.KVCache(cfg.slots, C, H, D, torch.bfloat16)
+    cache.set_table(slot_permutation(cfg.slots, seed=cfg.seed)[:n0])
+    for g in range(n0):
+        cache.refresh(g, kd[g * C:(g + 1) * C], vd[g * C:(g + 1) * C])
+    q, k, v = (dev_bf16(torch, a) for a in make_rollout_round(cfg, 0))
+    out = torch.empty_like(q)
+    lse = torch.empty((H, N * C), dtype=torch.float32, device="cuda")
+
+    def one(r, t=None):
+        first = r + Hs
+        if t:
+            t.mark(0)
+        wf.rope3d(q, first, fpc, gh, gw, split)
+        wf.rope3d(k, first, fpc, gh, gw, split)
+        if t:
+            t.mark(1)
+        cache.append(k[(N - 1) * C:], v[(N - 1) * C:])
+        for j in range(N - 1):
+            cache.refresh(Hs + j, k[j * C:(j + 1) * C], v[j * C:(j + 1) * C])
+        if t:
+            t.mark(2)
+        wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, lse=lse)
+        if t:
+            t.mark(3)
+        cache.evict(1)
+
+    for r in range(warmup):
+        one(r)
+    timers = [Timer(torch, stream, 4) for _ in range(rounds)]
+    torch.cuda.synchronize()
+    for r in range(rounds):
+        one(warmup + r, timers[r])
+    torch.cuda.synchronize()
+    rope = np.array([t.ms(0, 1) for t in timers])
+    kvw = np.array([t.ms(1, 2) for t in timers])
+    attn = np.array([t.ms(2, 3) for t in timers])
+    tot = rope + kvw + attn
+    rope_bytes = 2 * 2 * N * chunk_bytes(cfg)        # Q and K, read + write
+    kv_bytes = 4 * N * chunk_bytes(cfg)              # N chunks of K and V, read + write
+    eff = effective_flops(cfg)
+    return {
+        "workload": f"{cfg.name}: {cfg.description}",
+        "rounds_timed": rounds,
+        "round": ms_summary(tot),
+        "hot_path_rounds_per_s": 1e3 / float(np.median(tot)),
+        "attention": {**ms_summary(attn), "tflops_median": eff / (np.median(attn) / 1e3) / 1e12,
+                      "frac_of_bf16_peak": eff / (np.median(attn) / 1e3) / 1e12 / BF16_DENSE_TFLOPS},
+        "rope3d_q_and_k": {**ms_summary(rope), "gbs_median": rope_bytes / (np.median(rope) / 1e3) / 1e9,
+                           "frac_of_hbm_peak": rope_bytes / (np.median(rope) / 1e3) / 1e9 / HBM_GBS,
+                           "bytes": rope_bytes},
+        "kv_writes": {**ms_summary(kvw), "gbs_median": kv_bytes / (np.median(kvw) / 1e3) / 1e9, "bytes": kv_bytes},
+    }
+
+
+def bench_i8qk(torch, wf, cfg, steps, warmup, stream):
+    """14B-shaped int8-QK round: quantization kernels + int8 attention, one C call."""
+    C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
+    inp = make_round_inputs(cfg)
+    q = dev_bf16(torch, inp.q)
+    cache = wf.KVCache(Hs + N, C, H, D, torch.bfloat16)
+    for src_k, src_v, n in ((inp.k_hist, inp.v_hist, Hs), (inp.k_in, inp.v_in, N)):
+        kk, vv = dev_bf16(torch, src_k), dev_bf16(torch, src_v)
+        for c in range(n):
+            cache.append(kk[c * C:(c + 1) * C], vv[c * C:(c + 1) * C])
+        torch.cuda.synchronize()
+        del kk, vv
+    del inp
+    ws = torch.empty(wf.attn_i8qk_workspace_bytes(cache, N), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((H, N * C), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        wf.chunk_causal_attn_fwd_i8qk(q, cache, N, cfg.scale, workspace=ws, out=out, lse=lse)
+    timers = [Timer(torch, stream, 2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for t in timers:
+        t.mark(0)
+        wf.chunk_causal_attn_fwd_i8qk(q, cache, N, cfg.scale, workspace=ws, out=out, lse=lse)
+        t.mark(1)
+    torch.cuda.synchronize()
+    ms = np.array([t.ms(0, 1) for t in timers])
+    eff = effective_flops(cfg)
+    tops = eff / (np.median(ms) / 1e3) / 1e12
+    return {
+        "workload": f"{cfg.name}: {cfg.description}",
+        "call": "quantize K - mean and Q (3 kernels) + int8-QK attention",
+        **ms_summary(ms),
+        "effective_tops_median": tops,
+        "peak_mixed_tops": I8QK_MIXED_PEAK,
+        "frac_of_mixed_peak": tops / I8QK_MIXED_PEAK,
+        "frac_of_bf16_peak": tops / BF16_DENSE_TFLOPS,
+        "chunk_rounds_per_s": 1e3 / float(np.median(ms)),
+    }
+
+
+def copy_probe(torch, mib: int):
+    """A plain device-to-device copy of known size, for calibrating HBM byte counters."""
+    n = mib * 1024 * 1024 // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"[bench] copy probe: {n * 2} bytes x 3", file=sys.stderr, flush=True)
 
 
 def main():
@@ -106,14 +317,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="wan13b_4step", choices=sorted(CONFIGS))
     ap.add_argument("--cpu-rows", type=int, default=4680, help="query rows per chunk in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the rollout and int8-QK measurements")
+    ap.add_argument("--copy-probe-mib", type=int, default=0, help="run a plain copy of this size first")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -122,61 +337,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-
-    cfg = CONFIGS[args.config]
-    if cfg.int8_qk or cfg.rope or cfg.dtype != "bf16":
-        print("bench.py times the bf16 round without RoPE; pick wan13b_4step or step5_refresh", file=sys.stderr)
-        sys.exit(2)
-    C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
-    dt = torch.bfloat16
-    inp = make_round_inputs(cfg)
-
-    def dev(a):
-        return torch.from_numpy(a).to("cuda").to(dt)
-
-    q, k_in, v_in = dev(inp.q), dev(inp.k_in), dev(inp.v_in)
-    k_hist, v_hist = dev(inp.k_hist), dev(inp.v_hist)
-    kc = [k_in[j * C:(j + 1) * C] for j in range(N)]
-    vc = [v_in[j * C:(j + 1) * C] for j in range(N)]
-
-    # Steady state between rounds: n_hist history chunks + the N-1 continuing in-flight chunks.
-    cache = wf.KVCache(Hs + N, C, H, D, dt)
-    for c in range(Hs):
-        cache.append(k_hist[c * C:(c + 1) * C], v_hist[c * C:(c + 1) * C])
-    for j in range(N - 1):
-        cache.append(kc[j], vc[j])
-    out = torch.empty_like(q)
-    lse = torch.empty((H, N * C), dtype=torch.float32, device="cuda")
+    wf.lib()  # fails loudly when the HIP library is missing
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)
 
-    def step(ev=None):
-        cache.append(kc[N - 1], vc[N - 1])              # new noisiest chunk
-        for j in range(N - 1):                          # this round's K/V of the continuing chunks
-            cache.refresh(Hs + j, kc[j], vc[j])
-        if ev is not None:
-            ev[0].record(stream)
-        wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, lse=lse)
-        if ev is not None:
-            ev[1].record(stream)
-        cache.evict(1)                                  # refresh chunk is history from now on
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    attn_ms = np.array([a.elapsed_time(b) for a, b in events])
-    ms_per_step = wall * 1e3 / args.steps
+    cfg = CONFIGS["wan13b_4step"]
+    inp, ms_per_step, kv_ms, attn_ms = bench_round(torch, wf, cfg, args.steps, args.warmup, stream)
+    print(f"[bench] {cfg.name}: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     eff = effective_flops(cfg)
-    attn_avg_s = float(attn_ms.mean()) / 1e3
-    achieved = eff / attn_avg_s / 1e12
+    attn_s = float(np.mean(attn_ms)) / 1e3
+    achieved = eff / attn_s / 1e12
+    kv_bytes = 4 * cfg.n_inflight * chunk_bytes(cfg)
     traffic = load_traffic(cfg.name)
     res = {
         "metric": METRIC,
@@ -193,28 +366,41 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {cfg.description}",
-            "heads": H, "head_dim": D, "chunk_tokens": C, "n_inflight": N, "n_hist": Hs,
-            "query_tokens": N * C, "visible_keys_max": (Hs + N) * C,
+            "heads": cfg.n_heads, "head_dim": cfg.head_dim, "chunk_tokens": cfg.chunk_tokens,
+            "n_inflight": cfg.n_inflight, "n_hist": cfg.n_hist,
+            "query_tokens": cfg.nq, "visible_keys_max": cfg.nkv,
             "effective_flops_per_round": eff,
+            "executed_flops_per_round": executed_flops(cfg),
             "step": "kv append (1 chunk) + kv refresh (N-1 chunks) + attention + evict",
         },
         "chunk_rounds_per_s": 1e3 / ms_per_step,
         "attention": {
-            "ms_mean": float(attn_ms.mean()), "ms_median": float(np.median(attn_ms)),
-            "ms_p10": float(np.percentile(attn_ms, 10)), "ms_p90": float(np.percentile(attn_ms, 90)),
-            "tflops": achieved, "frac_of_bf16_peak": achieved / MI355X_BF16_DENSE_TFLOPS,
-            "rounds_per_s": 1.0 / attn_avg_s,
+            **ms_summary(attn_ms),
+            "tflops": achieved, "frac_of_bf16_peak": achieved / BF16_DENSE_TFLOPS,
+            "executed_tflops": executed_flops(cfg) / attn_s / 1e12,
+            "rounds_per_s": 1.0 / attn_s,
         },
+        "kv_writes": {**ms_summary(kv_ms), "bytes": kv_bytes,
+                      "gbs_median": kv_bytes / (np.median(kv_ms) / 1e3) / 1e9,
+                      "frac_of_hbm_peak": kv_bytes / (np.median(kv_ms) / 1e3) / 1e9 / HBM_GBS},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_kernel<128,8>",
+            "kernel": ATTN_KERNEL,
             "achieved": achieved,
-            "peak": MI355X_BF16_DENSE_TFLOPS,
+            "peak": BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": achieved / MI355X_BF16_DENSE_TFLOPS,
+            "frac": achieved / BF16_DENSE_TFLOPS,
             "traffic": traffic,
+            "algorithmic_bytes_per_launch": attention_min_bytes(cfg),
+            "timing": "hip events on the launch stream around each attention launch, mean over the timed steps",
         },
     }
+    if not args.no_extras:
+        res["rollout"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream)
+        print("[bench] rollout done", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        res["i8qk"] = bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], 20, 3, stream)
+        print("[bench] int8-QK done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
     print(json.dumps(res), flush=True)

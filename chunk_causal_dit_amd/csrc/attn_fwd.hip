@@ -108,11 +108,28 @@ struct Work {
   int j, h, qt;
 };
 
-// Longest-first order: query chunk N-1 sees the most keys, so its tiles go first.
+constexpr int kXcds = 8;  // workgroup i of a launch runs on XCD i % 8; each XCD has its own L2
+
+// Work item of workgroup b. Items are numbered longest-first (query chunk
+// N-1 sees the most keys), then by head, then by query tile. The T query
+// tiles of one (chunk, head) read the same K/V tiles in the same order, so
+// they are placed on one XCD, where they share its L2: in every run of
+// 8*T consecutive workgroups, XCD x takes the T tiles of one (chunk, head),
+// alternating direction from run to run (which evens out the work per XCD
+// across the longest-first order). The last partial run keeps the plain order.
 __device__ __forceinline__ Work decode_block(int b, int N, int H, int T) {
+  int item = b;
+  const int run = kXcds * T;
+  const int full = (N * H * T) / run * run;
+  if (b < full) {
+    const int s = b / run, in = b - s * run;
+    int x = in % kXcds;
+    if (s & 1) x = kXcds - 1 - x;
+    item = s * run + x * T + in / kXcds;
+  }
   const int per = H * T;
-  const int cls = b / per;
-  const int rem = b - cls * per;
+  const int cls = item / per;
+  const int rem = item - cls * per;
   Work w;
   w.j = N - 1 - cls;
   w.h = rem / T;

@@ -1,0 +1,119 @@
+"""Summaries of rocprofv3 output for the kernels of the round.
+
+    python -m chunk_causal_dit_amd.profiling stats  <run_kernel_stats.csv> --cmd "<command>" --out <file.md>
+    python -m chunk_causal_dit_amd.profiling traffic --fetch <fetch counter_collection.csv>
+        --write <write counter_collection.csv> --kernel <name substring> --copy-bytes <bytes>
+        --cmd "<command>" --source <kernel .hip file> --out <file.json>
+
+``stats`` turns a ``--kernel-trace --stats`` run into a short markdown table
+(calls, average / min / max duration per kernel). ``traffic`` turns two
+``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs into HBM bytes per launch of
+one kernel. Both counters are read in KiB per dispatch; each is calibrated by
+what it reads for a plain device-to-device copy of known size in the same run
+(the largest dispatch whose name contains "copy"): factor = counter KiB * 1024
+/ copy bytes, and the kernel's bytes = counter KiB * 1024 / factor. The JSON
+records the sha256 prefix of the kernel source, so a reader can tell when the
+counters no longer describe the current kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import sys
+from typing import Dict, List
+
+
+def _rows(path: str) -> List[dict]:
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def short_name(name: str, width: int = 90) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def stats_markdown(stats_csv: str, cmd: str, top: int = 12) -> str:
+    rows = _rows(stats_csv)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"Command: `{cmd}`", "",
+           "| kernel | calls | avg us | min us | max us | % of GPU time |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for r in rows[:top]:
+        out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(path: str, counter: str) -> Dict[int, dict]:
+    """dispatch id -> {name, value (summed over the counter's instances), grid}."""
+    per: Dict[int, dict] = {}
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        rec = per.setdefault(d, {"name": r["Kernel_Name"], "value": 0.0, "grid": int(r["Grid_Size"])})
+        rec["value"] += float(r["Counter_Value"])
+    return per
+
+
+def calibrated_bytes(path: str, counter: str, kernel: str, copy_bytes: int):
+    per = _per_dispatch(path, counter)
+    copies = [d for d in per.values() if "copy" in d["name"].lower()]
+    if not copies:
+        raise SystemExit(f"{path}: no copy dispatch to calibrate {counter}")
+    ref = max(copies, key=lambda d: d["value"])
+    factor = ref["value"] * 1024.0 / copy_bytes
+    vals = [d["value"] for d in per.values() if kernel in d["name"]]
+    if not vals:
+        raise SystemExit(f"{path}: no dispatch of {kernel}")
+    kib = sum(vals) / len(vals)
+    return {"counter_kib_per_launch": kib, "launches": len(vals), "copy_counter_kib": ref["value"],
+            "factor": factor, "bytes_per_launch": kib * 1024.0 / factor}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    s.add_argument("--title", default="rocprofv3 --kernel-trace --stats")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--algorithmic-bytes", type=float, default=None)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.what == "stats":
+        text = f"# {a.title}\n\n" + stats_markdown(a.csv, a.cmd)
+        open(a.out, "w").write(text)
+        print(text)
+        return
+    fetch = calibrated_bytes(a.fetch, "FETCH_SIZE", a.kernel, a.copy_bytes)
+    write = calibrated_bytes(a.write, "WRITE_SIZE", a.kernel, a.copy_bytes)
+    rec = {
+        "kernel": a.kernel,
+        "command": a.cmd,
+        "kernel_source_sha256_16": hashlib.sha256(open(a.source, "rb").read()).hexdigest()[:16],
+        "copy_bytes": a.copy_bytes,
+        "fetch": fetch,
+        "write": write,
+        "hbm_bytes_per_launch": fetch["bytes_per_launch"] + write["bytes_per_launch"],
+        "algorithmic_bytes_per_launch": a.algorithmic_bytes,
+    }
+    json.dump(rec, open(a.out, "w"), indent=1)
+    json.dump(rec, sys.stdout, indent=1)
+    print()
+
+
+if __name__ == "__main__":
+    main()
