@@ -58,11 +58,12 @@ def effective_flops(cfg: RoundConfig) -> float:
     return 4.0 * cfg.head_dim * cfg.n_heads * effective_pairs_per_head(cfg)
 
 
-def executed_flops(cfg: RoundConfig, q_rows: int = 256, key_tile: int = 64) -> float:
-    """FLOPs the kernel issues: whole query tiles of q_rows rows (the tail padded), whole key
-    tiles of every visible chunk (the tail tile padded)."""
+def executed_flops(cfg: RoundConfig, wave_rows: int = 32, key_tile: int = 64) -> float:
+    """FLOPs the kernel issues: each wave holds 32 query rows (a wave past the chunk end
+    issues nothing; the last one pads its rows) and covers whole 64-key tiles of every
+    visible chunk (the tail tile padded)."""
     C = cfg.chunk_tokens
-    qpad = -(-C // q_rows) * q_rows
+    qpad = -(-C // wave_rows) * wave_rows
     kpad = -(-C // key_tile) * key_tile
     return 4.0 * cfg.head_dim * cfg.n_heads * sum(qpad * (cfg.n_hist + j + 1) * kpad for j in range(cfg.n_inflight))
 
@@ -196,10 +197,11 @@ def bench_round(torch, wf, cfg, steps, warmup, stream):
     return inp, wall * 1e3 / steps, kv_ms, attn_ms
 
 
-def bench_rollout(torch, wf, cfg, rounds, warmup, stream):
-    """Long-rollout steady state: per round rope3d(Q), rope3d(K), append, refresh, attention,
-    evict, on a permuted 12-slot ring. Timing only (the values are those of round 0, rotated
-    again every round)."""
+def bench_rollout(torch, wf, cfg, rounds, warmup, stream, fused=False):
+    """Long-rollout steady state on a permuted 12-slot ring: per round rope3d(Q), rope3d(K),
+    append, refresh, attention, evict; with fused=True, K is rotated inside the cache writes
+    (append_rope / refresh_rope) instead. Timing only (the values are those of round 0,
+    rotated again every round)."""
     from workloads import slot_permutation
     C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
     fpc, gh, gw, split = cfg.frames_per_chunk, cfg.grid_h, cfg.grid_w, cfg.rope_split
@@ -209,6 +211,8 @@ def bench_rollout(torch, wf, cfg, rounds, warmup, stream):
     n0 = Hs + N - 1
     cache = wf.KVCache(cfg.slots, C, H, D, torch.bfloat16)
     cache.set_table(slot_permutation(cfg.slots, seed=cfg.seed)[:n0])
+    if fused:
+        cache.set_rope(fpc, gh, gw, split)
     for g in range(n0):
         cache.refresh(g, kd[g * C:(g + 1) * C], vd[g * C:(g + 1) * C])
     q, k, v = (dev_bf16(torch, a) for a in make_rollout_round(cfg, 0))
@@ -220,12 +224,18 @@ def bench_rollout(torch, wf, cfg, rounds, warmup, stream):
         if t:
             t.mark(0)
         wf.rope3d(q, first, fpc, gh, gw, split)
-        wf.rope3d(k, first, fpc, gh, gw, split)
+        if not fused:
+            wf.rope3d(k, first, fpc, gh, gw, split)
         if t:
             t.mark(1)
-        cache.append(k[(N - 1) * C:], v[(N - 1) * C:])
-        for j in range(N - 1):
-            cache.refresh(Hs + j, k[j * C:(j + 1) * C], v[j * C:(j + 1) * C])
+        if fused:
+            cache.append_rope(k[(N - 1) * C:], v[(N - 1) * C:], first + N - 1)
+            for j in range(N - 1):
+                cache.refresh_rope(Hs + j, k[j * C:(j + 1) * C], v[j * C:(j + 1) * C], first + j)
+        else:
+            cache.append(k[(N - 1) * C:], v[(N - 1) * C:])
+            for j in range(N - 1):
+                cache.refresh(Hs + j, k[j * C:(j + 1) * C], v[j * C:(j + 1) * C])
         if t:
             t.mark(2)
         wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, lse=lse)
@@ -244,17 +254,18 @@ def bench_rollout(torch, wf, cfg, rounds, warmup, stream):
     kvw = np.array([t.ms(1, 2) for t in timers])
     attn = np.array([t.ms(2, 3) for t in timers])
     tot = rope + kvw + attn
-    rope_bytes = 2 * 2 * N * chunk_bytes(cfg)        # Q and K, read + write
+    rope_bytes = (1 if fused else 2) * 2 * N * chunk_bytes(cfg)  # Q (and K unless fused), read + write
     kv_bytes = 4 * N * chunk_bytes(cfg)              # N chunks of K and V, read + write
     eff = effective_flops(cfg)
     return {
         "workload": f"{cfg.name}: {cfg.description}",
+        "producer": "K rotated inside the cache writes" if fused else "rope3d on Q and K, then the cache writes",
         "rounds_timed": rounds,
         "round": ms_summary(tot),
         "hot_path_rounds_per_s": 1e3 / float(np.median(tot)),
         "attention": {**ms_summary(attn), "tflops_median": eff / (np.median(attn) / 1e3) / 1e12,
                       "frac_of_bf16_peak": eff / (np.median(attn) / 1e3) / 1e12 / BF16_DENSE_TFLOPS},
-        "rope3d_q_and_k": {**ms_summary(rope), "gbs_median": rope_bytes / (np.median(rope) / 1e3) / 1e9,
+        ("rope3d_q" if fused else "rope3d_q_and_k"): {**ms_summary(rope), "gbs_median": rope_bytes / (np.median(rope) / 1e3) / 1e9,
                            "frac_of_hbm_peak": rope_bytes / (np.median(rope) / 1e3) / 1e9 / HBM_GBS,
                            "bytes": rope_bytes},
         "kv_writes": {**ms_summary(kvw), "gbs_median": kv_bytes / (np.median(kvw) / 1e3) / 1e9, "bytes": kv_bytes},
@@ -301,6 +312,37 @@ def bench_i8qk(torch, wf, cfg, steps, warmup, stream):
     }
 
 
+def bench_power(torch, wf, cfg, seconds):
+    """Board power while the headline attention runs back to back, and energy per launch."""
+    from chunk_causal_dit_amd.profiling import sample_power
+    C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
+    inp = make_round_inputs(cfg)
+    q = dev_bf16(torch, inp.q)
+    cache = wf.KVCache(Hs + N, C, H, D, torch.bfloat16)
+    for src_k, src_v, n in ((inp.k_hist, inp.v_hist, Hs), (inp.k_in, inp.v_in, N)):
+        kk, vv = dev_bf16(torch, src_k), dev_bf16(torch, src_v)
+        for c in range(n):
+            cache.append(kk[c * C:(c + 1) * C], vv[c * C:(c + 1) * C])
+    out = torch.empty_like(q)
+    reps = 20
+
+    def run():
+        for _ in range(reps):
+            wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, with_lse=False)
+
+    run()
+    torch.cuda.synchronize()
+    rec = sample_power(run, torch.cuda.synchronize, seconds)
+    if rec is None:
+        return {"available": False}
+    launches = rec["calls"] * reps
+    s_per = rec["seconds"] / launches
+    return {"available": True, "watts": rec["watts"], "launches": launches, "ms_per_launch": s_per * 1e3,
+            "joules_per_launch": rec["watts"] * s_per,
+            "effective_gflop_per_joule": effective_flops(cfg) / (rec["watts"] * s_per) / 1e9,
+            "sensor": rec["sensor"]}
+
+
 def copy_probe(torch, mib: int):
     """A plain device-to-device copy of known size, for calibrating HBM byte counters."""
     n = mib * 1024 * 1024 // 2
@@ -321,6 +363,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the rollout and int8-QK measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0, help="run a plain copy of this size first")
+    ap.add_argument("--power-seconds", type=float, default=3.0,
+                    help="seconds of back-to-back attention launches with the board power sensor read (0: off)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -395,8 +439,11 @@ def main():
             "timing": "hip events on the launch stream around each attention launch, mean over the timed steps",
         },
     }
+    if args.power_seconds > 0:
+        res["power"] = bench_power(torch, wf, cfg, args.power_seconds)
     if not args.no_extras:
         res["rollout"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream)
+        res["rollout_fused"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream, fused=True)
         print("[bench] rollout done", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         res["i8qk"] = bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], 20, 3, stream)

@@ -58,6 +58,9 @@ _SIGNATURES = {
     "wf_kv_get_table": (_c_int, [_vp, ctypes.POINTER(_c_int), _c_int, ctypes.POINTER(_c_int)]),
     "wf_rope3d": (_c_int, [_vp] + [_c_int] * 11 + [ctypes.c_float, _vp]),
     "wf_chunk_causal_attn_fwd": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp]),
+    "wf_kv_set_rope": (_c_int, [_vp] + [_c_int] * 6 + [ctypes.c_float]),
+    "wf_kv_append_rope": (_c_int, [_vp, _vp, _vp, _c_int, _vp, ctypes.POINTER(_c_int)]),
+    "wf_kv_refresh_rope": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _vp]),
     "wf_attn_i8qk_workspace_bytes": (_c_size, [_vp, _c_int]),
     "wf_chunk_causal_attn_fwd_i8qk": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp]),
     "wf_status_str": (ctypes.c_char_p, [_c_int]),
@@ -183,6 +186,25 @@ class KVCache:
     def refresh(self, logical_idx: int, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
         _check(lib().wf_kv_refresh(self.handle, logical_idx, self._chunk(k, "k"), self._chunk(v, "v"),
                                    _vp(_stream(stream))), "wf_kv_refresh")
+
+    def set_rope(self, frames_per_chunk: int, grid_h: int, grid_w: int,
+                 split: Tuple[int, int, int] = (44, 42, 42), theta: float = 10000.0) -> None:
+        """RoPE geometry for append_rope / refresh_rope (same convention as rope3d)."""
+        _check(lib().wf_kv_set_rope(self.handle, frames_per_chunk, grid_h, grid_w, split[0], split[1], split[2],
+                                    float(theta)), "wf_kv_set_rope")
+
+    def append_rope(self, k: torch.Tensor, v: torch.Tensor, global_chunk: int, stream=None) -> int:
+        """append with K rotated at the positions of global chunk global_chunk (k is not modified)."""
+        slot = ctypes.c_int(-1)
+        _check(lib().wf_kv_append_rope(self.handle, self._chunk(k, "k"), self._chunk(v, "v"), global_chunk,
+                                       _vp(_stream(stream)), ctypes.byref(slot)), "wf_kv_append_rope")
+        return slot.value
+
+    def refresh_rope(self, logical_idx: int, k: torch.Tensor, v: torch.Tensor, global_chunk: int,
+                     stream=None) -> None:
+        """refresh with K rotated at the positions of global chunk global_chunk."""
+        _check(lib().wf_kv_refresh_rope(self.handle, logical_idx, self._chunk(k, "k"), self._chunk(v, "v"),
+                                        global_chunk, _vp(_stream(stream))), "wf_kv_refresh_rope")
 
     def evict(self, n_oldest: int) -> None:
         _check(lib().wf_kv_evict(self.handle, n_oldest), "wf_kv_evict")

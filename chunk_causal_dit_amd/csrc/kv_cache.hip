@@ -16,7 +16,15 @@
 // One workgroup handles one (64-token tile, head): it stages the tile's K and
 // V rows in LDS (coalesced reads of the token-major source) and writes both
 // images with fully coalesced 16-byte stores. HBM-bound.
-#include "wf_internal.h"
+//
+// The fused write (append/refresh with RoPE) rotates K on its way into the
+// slot, so rotated K never makes a round trip through HBM. One workgroup
+// handles a slice of 256 / (pieces per row) tokens (16 for bf16 at head_dim
+// 128) of one head: each thread loads one 16-byte piece of K and of V,
+// rotates the K pairs (its own sin/cos), and the slice is written through LDS
+// as that key range of the tile images. Many small workgroups keep enough
+// loads in flight; the sin/cos work overlaps the memory latency.
+#include "rope_common.h"
 
 namespace {
 
@@ -81,6 +89,85 @@ __global__ __launch_bounds__(256) void kv_tile_kernel(const T* __restrict__ ksrc
   }
 }
 
+template <typename T, int D>
+__global__ __launch_bounds__(256) void kv_rope_tile_kernel(const T* __restrict__ ksrc, const T* __restrict__ vsrc,
+                                                           char* __restrict__ kdst, char* __restrict__ vdst, int C,
+                                                           int H, int s_pad, int g, int fpc, int gh, int gw,
+                                                           wf::RopeTable tab) {
+  constexpr int E = 16 / sizeof(T);    // elements per 16-byte piece
+  constexpr int PPR = D / E;           // pieces per token row
+  constexpr int TG = 256 / PPR;        // tokens per workgroup: one piece per thread
+  constexpr int PAIRS = E / 2;         // rotated pairs per piece
+  constexpr int KROW = PPR * 16 + 16;  // LDS row pitch (bytes) of the K slice
+  constexpr int VROW = D + 2;          // LDS row pitch (elements) of the V slice
+  constexpr int TILE = 64 * D * (int)sizeof(T);
+  static_assert(TG * PPR == 256 && 64 % TG == 0 && TG % E == 0, "tile slices must split evenly");
+  __shared__ __attribute__((aligned(16))) char kt[TG * KROW];
+  __shared__ T vt[TG][VROW];
+  const int t0 = blockIdx.x * TG, h = blockIdx.y;
+  const int tile = t0 / 64, key0 = t0 % 64;
+  const int tid = threadIdx.x;
+  {  // load, rotate, stage: thread (row r, piece c)
+    const int r = tid / PPR, c = tid % PPR;
+    const int t = t0 + r;
+    u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+    if (t < C) {
+      const size_t off = ((size_t)t * H + h) * D + c * E;
+      kr = *reinterpret_cast<const u32x4*>(ksrc + off);
+      vr = *reinterpret_cast<const u32x4*>(vsrc + off);
+      float pos[3];
+      wf::rope_token_pos(g, t, fpc, gh, gw, pos);
+      T x[E];
+      __builtin_memcpy(x, &kr, 16);
+#pragma unroll
+      for (int k = 0; k < PAIRS; ++k) {
+        float sn, cs;
+        wf::rope_sincos(pos, tab, c * PAIRS + k, sn, cs);
+        wf::rope_rotate_pair(x[2 * k], x[2 * k + 1], cs, sn);
+      }
+      __builtin_memcpy(&kr, x, 16);
+    }
+    *reinterpret_cast<u32x4*>(kt + r * KROW + c * 16) = kr;
+    T vals[E];
+    __builtin_memcpy(vals, &vr, 16);
+#pragma unroll
+    for (int e = 0; e < E; ++e) vt[r][c * E + e] = vals[e];
+  }
+  __syncthreads();
+  const size_t tile_off = ((size_t)h * (s_pad / 64) + tile) * TILE;
+  {  // K image: piece p, keys key0 .. key0+TG-1 (TG contiguous 16-byte rows)
+    const int p = tid / TG, r = tid % TG;
+    *reinterpret_cast<u32x4*>(kdst + tile_off + p * (64 * 16) + (key0 + r) * 16) =
+        *reinterpret_cast<const u32x4*>(kt + r * KROW + p * 16);
+  }
+  {  // V image: group of E keys (key0/E + grp), dim d
+    const int grp = tid / D, d = tid % D;
+    T vals[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) vals[e] = vt[grp * E + e][d];
+    u32x4 raw;
+    __builtin_memcpy(&raw, vals, 16);
+    *reinterpret_cast<u32x4*>(vdst + tile_off + (key0 / E + grp) * (D * 16) + d * 16) = raw;
+  }
+}
+
+template <typename T>
+hipError_t launch_rope_tiles(const wf_kv_cache& kv, const void* k, const void* v, char* kdst, char* vdst, int g,
+                             hipStream_t s) {
+  const int tg = 256 * 16 / (int)sizeof(T) / kv.head_dim;      // tokens per workgroup (as in the kernel)
+  const dim3 grid((kv.chunk_tokens + 63) / 64 * (64 / tg), kv.n_heads);  // slices up to the end of the last tile
+  const T* kp = static_cast<const T*>(k);
+  const T* vp = static_cast<const T*>(v);
+  const wf::RopeConfig& rc = kv.rope;
+  if (kv.head_dim == 128)
+    kv_rope_tile_kernel<T, 128><<<grid, 256, 0, s>>>(kp, vp, kdst, vdst, kv.chunk_tokens, kv.n_heads, kv.s_pad, g,
+                                                        rc.fpc, rc.gh, rc.gw, rc.table);
+  else
+    kv_rope_tile_kernel<T, 64><<<grid, 256, 0, s>>>(kp, vp, kdst, vdst, kv.chunk_tokens, kv.n_heads, kv.s_pad, g,
+                                                       rc.fpc, rc.gh, rc.gw, rc.table);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_tiles(const wf_kv_cache& kv, const void* k, const void* v, char* kdst, char* vdst, hipStream_t s) {
   dim3 grid((kv.chunk_tokens + 63) / 64, kv.n_heads);
@@ -111,6 +198,15 @@ hipError_t launch_kv_write(const wf_kv_cache& kv, int slot, const void* k, const
   char* vdst = static_cast<char*>(kv.v_pool) + (size_t)slot * slot_bytes;
   if (kv.dtype == WF_BF16) return launch_tiles<__bf16>(kv, k, v, kdst, vdst, s);
   return launch_tiles<float>(kv, k, v, kdst, vdst, s);
+}
+
+hipError_t launch_kv_write_rope(const wf_kv_cache& kv, int slot, const void* k, const void* v, int global_chunk,
+                                hipStream_t s) {
+  const size_t slot_bytes = kv.slot_elems * kv.esize;
+  char* kdst = static_cast<char*>(kv.k_pool) + (size_t)slot * slot_bytes;
+  char* vdst = static_cast<char*>(kv.v_pool) + (size_t)slot * slot_bytes;
+  if (kv.dtype == WF_BF16) return launch_rope_tiles<__bf16>(kv, k, v, kdst, vdst, global_chunk, s);
+  return launch_rope_tiles<float>(kv, k, v, kdst, vdst, global_chunk, s);
 }
 
 }  // namespace wf

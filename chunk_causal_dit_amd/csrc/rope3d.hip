@@ -6,7 +6,7 @@
 // One thread owns 4 consecutive pairs (8 elements) of one token and applies
 // the same 4 rotations to that token's row in every head, so each sin/cos is
 // evaluated once per token rather than once per head. HBM-bound.
-#include "wf_internal.h"
+#include "rope_common.h"
 
 namespace {
 
@@ -46,29 +46,16 @@ __global__ __launch_bounds__(256) void rope3d_kernel(T* __restrict__ x, int n_to
   const int t = (int)(gid / GROUPS);
   const int grp = (int)(gid - (long long)t * GROUPS);
   const int chunk = fpc * gh * gw;
-  const int g = first_chunk + t / chunk;
-  const int u = t % chunk;
-  const int plane = gh * gw;
   float pos[3];
-  pos[0] = (float)(fpc * g + u / plane);
-  pos[1] = (float)((u / gw) % gh);
-  pos[2] = (float)(u % gw);
+  wf::rope_token_pos(first_chunk + t / chunk, t % chunk, fpc, gh, gw, pos);
   float cs[4], sn[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int pr = grp * 4 + k;
-    const float phi = pos[tab.axis[pr]] * tab.inv_freq[pr];
-    sincosf(phi, &sn[k], &cs[k]);
-  }
+  for (int k = 0; k < 4; ++k) wf::rope_sincos(pos, tab, grp * 4 + k, sn[k], cs[k]);
   T* row = x + (size_t)t * H * D + grp * 8;
   for (int h = 0; h < H; ++h, row += D) {
     Vec8<T> a = load8(row);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float x0 = (float)a.v[2 * k], x1 = (float)a.v[2 * k + 1];
-      a.v[2 * k] = (T)(x0 * cs[k] - x1 * sn[k]);
-      a.v[2 * k + 1] = (T)(x0 * sn[k] + x1 * cs[k]);
-    }
+    for (int k = 0; k < 4; ++k) wf::rope_rotate_pair(a.v[2 * k], a.v[2 * k + 1], cs[k], sn[k]);
     store8(row, a);
   }
 }

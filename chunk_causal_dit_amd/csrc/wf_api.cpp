@@ -159,27 +159,18 @@ WF_EXPORT int wf_kv_get_table(const wf_kv_cache* kv, int* slots, int cap, int* n
   return ok();
 }
 
-WF_EXPORT int wf_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dtype, int first_global_chunk,
-                        int frames_per_chunk, int grid_h, int grid_w, int d_t, int d_h, int d_w,
-                        float theta, void* stream) {
-  if (!x) return fail(WF_E_NULL, "wf_rope3d: NULL x");
-  if (!aligned(x, 16)) return fail(WF_E_SHAPE, "wf_rope3d: x must be 16-byte aligned");
-  if (dtype_size(dtype) == 0) return fail(WF_E_DTYPE, "wf_rope3d: unknown dtype %d", dtype);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(WF_E_UNSUPPORTED, "wf_rope3d: head_dim %d not supported", head_dim);
-  if (n_heads < 1 || frames_per_chunk < 1 || grid_h < 1 || grid_w < 1 || n_tokens < 0)
-    return fail(WF_E_SHAPE, "wf_rope3d: non-positive size");
+// Checks the RoPE geometry and builds its per-pair table (inverse frequency
+// rounded once to fp32, axis of the pair).
+static int rope_table(int head_dim, int frames_per_chunk, int grid_h, int grid_w, int d_t, int d_h, int d_w,
+                      float theta, RopeTable& t, const char* who) {
+  if (head_dim != 64 && head_dim != 128) return fail(WF_E_UNSUPPORTED, "%s: head_dim %d not supported", who, head_dim);
+  if (frames_per_chunk < 1 || grid_h < 1 || grid_w < 1) return fail(WF_E_SHAPE, "%s: non-positive grid", who);
   if (d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 || d_t + d_h + d_w != head_dim)
-    return fail(WF_E_SHAPE, "wf_rope3d: split %d/%d/%d must be even and sum to %d", d_t, d_h, d_w, head_dim);
-  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(WF_E_SHAPE, "wf_rope3d: theta must be positive");
-  const long long chunk = (long long)frames_per_chunk * grid_h * grid_w;
-  if (chunk > (1 << 20) || n_tokens % chunk)
-    return fail(WF_E_SHAPE, "wf_rope3d: n_tokens %d is not a multiple of the chunk (%lld)", n_tokens, chunk);
-  if (first_global_chunk < 0) return fail(WF_E_SHAPE, "wf_rope3d: negative chunk index");
-  if ((double)frames_per_chunk * (first_global_chunk + n_tokens / chunk + 1) > 16777216.0)
-    return fail(WF_E_SHAPE, "wf_rope3d: frame positions exceed the exact fp32 integer range");
-  if (n_tokens == 0) return ok();
-  RopeTable t{};
+    return fail(WF_E_SHAPE, "%s: split %d/%d/%d must be even and sum to %d", who, d_t, d_h, d_w, head_dim);
+  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(WF_E_SHAPE, "%s: theta must be positive", who);
+  if ((long long)frames_per_chunk * grid_h * grid_w > (1 << 20))
+    return fail(WF_E_SHAPE, "%s: chunk larger than 2^20 tokens", who);
+  t = RopeTable{};
   const int seg[3] = {d_t, d_h, d_w};
   int p = 0;
   for (int a = 0; a < 3; ++a)
@@ -187,9 +178,92 @@ WF_EXPORT int wf_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dt
       t.inv_freq[p] = (float)std::pow((double)theta, -2.0 * i / seg[a]);
       t.axis[p] = a;
     }
+  return WF_OK;
+}
+
+// Frame positions of chunks first .. first + n_chunks - 1 must be exact fp32 integers.
+static int rope_positions_ok(int frames_per_chunk, long long first, long long n_chunks, const char* who) {
+  if (first < 0) return fail(WF_E_SHAPE, "%s: negative chunk index", who);
+  if ((double)frames_per_chunk * (first + n_chunks + 1) > 16777216.0)
+    return fail(WF_E_SHAPE, "%s: frame positions exceed the exact fp32 integer range", who);
+  return WF_OK;
+}
+
+WF_EXPORT int wf_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dtype, int first_global_chunk,
+                        int frames_per_chunk, int grid_h, int grid_w, int d_t, int d_h, int d_w,
+                        float theta, void* stream) {
+  const char* who = "wf_rope3d";
+  if (!x) return fail(WF_E_NULL, "wf_rope3d: NULL x");
+  if (!aligned(x, 16)) return fail(WF_E_SHAPE, "wf_rope3d: x must be 16-byte aligned");
+  if (dtype_size(dtype) == 0) return fail(WF_E_DTYPE, "wf_rope3d: unknown dtype %d", dtype);
+  if (n_heads < 1 || n_tokens < 0) return fail(WF_E_SHAPE, "wf_rope3d: non-positive size");
+  RopeTable t;
+  int st = rope_table(head_dim, frames_per_chunk, grid_h, grid_w, d_t, d_h, d_w, theta, t, who);
+  if (st != WF_OK) return st;
+  const long long chunk = (long long)frames_per_chunk * grid_h * grid_w;
+  if (n_tokens % chunk)
+    return fail(WF_E_SHAPE, "wf_rope3d: n_tokens %d is not a multiple of the chunk (%lld)", n_tokens, chunk);
+  st = rope_positions_ok(frames_per_chunk, first_global_chunk, n_tokens / chunk, who);
+  if (st != WF_OK) return st;
+  if (n_tokens == 0) return ok();
   hipError_t e = launch_rope3d(x, n_tokens, n_heads, head_dim, dtype, first_global_chunk, frames_per_chunk,
                                grid_h, grid_w, t, static_cast<hipStream_t>(stream));
   return hip_status(e, "wf_rope3d");
+}
+
+WF_EXPORT int wf_kv_set_rope(wf_kv_cache* kv, int frames_per_chunk, int grid_h, int grid_w, int d_t, int d_h,
+                             int d_w, float theta) {
+  const char* who = "wf_kv_set_rope";
+  if (!kv) return fail(WF_E_NULL, "wf_kv_set_rope: NULL cache");
+  RopeTable t;
+  const int st = rope_table(kv->head_dim, frames_per_chunk, grid_h, grid_w, d_t, d_h, d_w, theta, t, who);
+  if (st != WF_OK) return st;
+  if ((long long)frames_per_chunk * grid_h * grid_w != kv->chunk_tokens)
+    return fail(WF_E_SHAPE, "wf_kv_set_rope: frames_per_chunk * grid_h * grid_w = %lld, chunk_tokens %d",
+                (long long)frames_per_chunk * grid_h * grid_w, kv->chunk_tokens);
+  kv->rope.on = true;
+  kv->rope.fpc = frames_per_chunk;
+  kv->rope.gh = grid_h;
+  kv->rope.gw = grid_w;
+  kv->rope.table = t;
+  return ok();
+}
+
+static int rope_write_checks(const wf_kv_cache* kv, const void* k, const void* v, int global_chunk, const char* who) {
+  if (!kv || !k || !v) return fail(WF_E_NULL, "%s: NULL argument", who);
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(WF_E_SHAPE, "%s: k and v must be 16-byte aligned", who);
+  if (!kv->rope.on) return fail(WF_E_UNSUPPORTED, "%s: no RoPE configured (wf_kv_set_rope)", who);
+  return rope_positions_ok(kv->rope.fpc, global_chunk, 1, who);
+}
+
+WF_EXPORT int wf_kv_append_rope(wf_kv_cache* kv, const void* k, const void* v, int global_chunk, void* stream,
+                                int* out_slot) {
+  const char* who = "wf_kv_append_rope";
+  int st = rope_write_checks(kv, k, v, global_chunk, who);
+  if (st != WF_OK) return st;
+  if (kv->free_slots.empty()) return fail(WF_E_FULL, "wf_kv_append_rope: no free slot (%d slots)", kv->n_slots);
+  if ((int)kv->table.size() >= WF_MAX_TABLE)
+    return fail(WF_E_FULL, "wf_kv_append_rope: table holds WF_MAX_TABLE entries");
+  const int slot = kv->free_slots.front();
+  hipError_t e = launch_kv_write_rope(*kv, slot, k, v, global_chunk, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, who);
+  kv->free_slots.pop_front();
+  kv->table.push_back(slot);
+  if (out_slot) *out_slot = slot;
+  return ok();
+}
+
+WF_EXPORT int wf_kv_refresh_rope(wf_kv_cache* kv, int logical_idx, const void* k, const void* v, int global_chunk,
+                                 void* stream) {
+  const char* who = "wf_kv_refresh_rope";
+  int st = rope_write_checks(kv, k, v, global_chunk, who);
+  if (st != WF_OK) return st;
+  if (logical_idx < 0 || logical_idx >= (int)kv->table.size())
+    return fail(WF_E_SLOT, "wf_kv_refresh_rope: logical index %d outside table of %zu", logical_idx,
+                kv->table.size());
+  hipError_t e =
+      launch_kv_write_rope(*kv, kv->table[logical_idx], k, v, global_chunk, static_cast<hipStream_t>(stream));
+  return hip_status(e, who);
 }
 
 static int fill_attn_params(const void* q, const wf_kv_cache* kv, int n_inflight, float scale, void* out,

@@ -13,6 +13,19 @@
 
 #define WF_EXPORT extern "C" __attribute__((visibility("default")))
 
+namespace wf {
+struct RopeTable {
+  float inv_freq[64];  // per pair, rounded once to fp32
+  int axis[64];        // 0 frame, 1 row, 2 column
+};
+// 3D RoPE applied to K by the fused cache writes (wf_kv_set_rope).
+struct RopeConfig {
+  bool on = false;
+  int fpc = 0, gh = 0, gw = 0;
+  RopeTable table{};
+};
+}  // namespace wf
+
 struct wf_kv_cache {
   void* k_pool = nullptr;
   void* v_pool = nullptr;
@@ -26,6 +39,7 @@ struct wf_kv_cache {
   size_t slot_elems = 0;    // n_heads * s_pad * head_dim elements per slot (each pool)
   std::vector<int> table;   // logical order, oldest first: physical slot ids
   std::deque<int> free_slots;
+  wf::RopeConfig rope;      // set by wf_kv_set_rope
 };
 
 namespace wf {
@@ -44,10 +58,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_kv_write(const wf_kv_cache& kv, int slot, const void* k, const void* v,
                            hipStream_t s);
 
-struct RopeTable {
-  float inv_freq[64];
-  int axis[64];
-};
+hipError_t launch_kv_write_rope(const wf_kv_cache& kv, int slot, const void* k, const void* v, int global_chunk,
+                                hipStream_t s);
+
 hipError_t launch_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dtype,
                          int first_global_chunk, int frames_per_chunk, int grid_h, int grid_w,
                          const RopeTable& table, hipStream_t s);

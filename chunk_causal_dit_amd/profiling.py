@@ -20,10 +20,14 @@ from __future__ import annotations
 import argparse
 import collections
 import csv
+import glob
 import hashlib
 import json
+import os
 import sys
-from typing import Dict, List
+import threading
+import time
+from typing import Callable, Dict, List, Optional
 
 
 def _rows(path: str) -> List[dict]:
@@ -73,6 +77,54 @@ def calibrated_bytes(path: str, counter: str, kernel: str, copy_bytes: int):
     kib = sum(vals) / len(vals)
     return {"counter_kib_per_launch": kib, "launches": len(vals), "copy_counter_kib": ref["value"],
             "factor": factor, "bytes_per_launch": kib * 1024.0 / factor}
+
+
+def hwmon_power_paths() -> List[str]:
+    """Board power sensors (microwatts) of the GPUs visible under /sys/class/drm."""
+    paths = []
+    for h in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        for name in ("power1_average", "power1_input"):
+            p = os.path.join(h, name)
+            if os.path.exists(p):
+                paths.append(p)
+                break
+    return paths
+
+
+def sample_power(run: Callable[[], None], sync: Callable[[], None], seconds: float = 3.0,
+                 period: float = 0.01) -> Optional[dict]:
+    """Calls run() repeatedly for about `seconds` (sync() after each call) while a thread reads
+    the board power sensor; returns mean watts (first quarter of the samples dropped as
+    ramp-up), calls made and wall seconds, or None when no sensor is readable."""
+    paths = hwmon_power_paths()
+    if not paths:
+        return None
+    path = paths[0]
+    samples: List[float] = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                samples.append(float(open(path).read()) * 1e-6)
+            except (OSError, ValueError):
+                pass
+            time.sleep(period)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    calls, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        run()
+        sync()
+        calls += 1
+    wall = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    kept = samples[len(samples) // 4:]
+    if not kept:
+        return None
+    return {"watts": sum(kept) / len(kept), "calls": calls, "seconds": wall, "sensor": path}
 
 
 def main(argv=None):

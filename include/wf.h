@@ -147,6 +147,30 @@ int wf_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dtype, int f
               void* stream);
 
 /* ------------------------------------------------------------------------
+ * Cache writes with RoPE on K (fused producer). They write the same slot
+ * contents as wf_rope3d applied to a copy of k (chunk index global_chunk,
+ * the convention above) followed by wf_kv_append / wf_kv_refresh, bit for bit,
+ * but K is rotated on its way into the slot: rotated K is never stored
+ * token-major, which saves one write and one read of K per chunk. k and v are
+ * not modified; V is written unrotated.
+ * ------------------------------------------------------------------------ */
+
+/* Sets the RoPE geometry of the cache (frames_per_chunk * grid_h * grid_w must
+ * equal chunk_tokens; split and theta as for wf_rope3d). Host-only; may be
+ * called again to change it. */
+int wf_kv_set_rope(wf_kv_cache* kv, int frames_per_chunk, int grid_h, int grid_w, int d_t, int d_h, int d_w,
+                   float theta);
+
+/* wf_kv_append with K rotated at the positions of global chunk global_chunk
+ * (>= 0). WF_E_UNSUPPORTED when no geometry was set. */
+int wf_kv_append_rope(wf_kv_cache* kv, const void* k, const void* v, int global_chunk, void* stream,
+                      int* out_slot);
+
+/* wf_kv_refresh with K rotated at the positions of global chunk global_chunk. */
+int wf_kv_refresh_rope(wf_kv_cache* kv, int logical_idx, const void* k, const void* v, int global_chunk,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Chunk-wise causal attention of one round (the round's hot loop).
  * q, out: [n_inflight*chunk_tokens][n_heads][head_dim] in the cache dtype;
  * query chunk j (0 = refresh chunk) reads the first n_hist + j + 1 table

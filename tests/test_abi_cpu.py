@@ -54,7 +54,7 @@ def test_exports_match_header(L):
     declared = wf.header_symbols()
     exported = wf.exported_symbols()
     assert declared == exported, (sorted(set(declared) - set(exported)), sorted(set(exported) - set(declared)))
-    assert len(declared) == 15
+    assert len(declared) == 18
 
 
 def test_version_and_status_strings(L):
@@ -187,6 +187,26 @@ def test_rope_argument_errors(L):
     assert r(x, 4, 1, 128, 5, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_DTYPE
     assert r(x, 4, 1, 128, 1, -1, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_SHAPE
     assert r(x, 0, 1, 128, 1, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_OK  # nothing to do
+
+
+def test_fused_rope_write_argument_errors(L):
+    """set_rope geometry checks; append_rope/refresh_rope refuse before any launch and leave the table as is."""
+    h, pools = make_cache(L, n_slots=3, C=60, H=2, D=128)
+    k = ctypes.c_void_p(pools.k.value)
+    slot = ctypes.c_int(-1)
+    assert L.wf_kv_append_rope(h, k, k, 0, None, ctypes.byref(slot)) == WF_E_UNSUPPORTED  # no geometry yet
+    assert L.wf_kv_set_rope(None, 3, 4, 5, 44, 42, 42, 1e4) == WF_E_NULL
+    assert L.wf_kv_set_rope(h, 3, 4, 4, 44, 42, 42, 1e4) == WF_E_SHAPE   # 3*4*4 != 60 tokens
+    assert L.wf_kv_set_rope(h, 3, 4, 5, 44, 42, 40, 1e4) == WF_E_SHAPE   # split does not sum to 128
+    assert L.wf_kv_set_rope(h, 3, 4, 5, 44, 42, 42, 0.0) == WF_E_SHAPE
+    assert L.wf_kv_set_rope(h, 3, 4, 5, 44, 42, 42, 1e4) == WF_OK
+    assert L.wf_kv_append_rope(h, None, k, 0, None, ctypes.byref(slot)) == WF_E_NULL
+    assert L.wf_kv_append_rope(h, ctypes.c_void_p(pools.k.value + 4), k, 0, None, None) == WF_E_SHAPE
+    assert L.wf_kv_append_rope(h, k, k, -1, None, None) == WF_E_SHAPE  # negative chunk index
+    assert L.wf_kv_append_rope(h, k, k, 1 << 23, None, None) == WF_E_SHAPE  # frames beyond exact fp32
+    assert L.wf_kv_refresh_rope(h, 0, k, k, 0, None) == WF_E_SLOT  # empty table
+    assert table(L, h) == [] and slot.value == -1
+    L.wf_kv_cache_destroy(h)
 
 
 def test_no_gpu_launch_fails_cleanly(L):
