@@ -29,6 +29,14 @@ def require_gpu():
     return wf
 
 
+def round_like(dtype: str):
+    """Float32 -> values representable in dtype (bf16: nearest even), as float32 arrays."""
+    from workloads import round_to_bf16
+    if dtype == "bf16":
+        return lambda a: round_to_bf16(np.asarray(a, dtype=np.float32))
+    return lambda a: np.asarray(a, dtype=np.float32)
+
+
 def torch_dtype(name: str):
     return torch.bfloat16 if name == "bf16" else torch.float32
 
