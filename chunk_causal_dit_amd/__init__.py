@@ -25,13 +25,14 @@ __all__ = [
     "WFError", "lib", "library_path", "exported_symbols", "header_symbols",
     "WF_F32", "WF_BF16", "KVCache", "kv_pool_bytes", "rope3d",
     "chunk_causal_attn_fwd", "attn_i8qk_workspace_bytes", "chunk_causal_attn_fwd_i8qk",
+    "quant_rows_i8", "gemm_w8a8", "WF_I32",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 HEADER = os.path.join(_ROOT, "include", "wf.h")
 
-WF_F32, WF_BF16 = 0, 1
+WF_F32, WF_BF16, WF_I32 = 0, 1, 2
 WF_KV_ADOPT, WF_KV_ZERO_FILL = 0, 1
 _DTYPE = {torch.float32: WF_F32, torch.bfloat16: WF_BF16}
 
@@ -63,6 +64,8 @@ _SIGNATURES = {
     "wf_kv_refresh_rope": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _vp]),
     "wf_attn_i8qk_workspace_bytes": (_c_size, [_vp, _c_int]),
     "wf_chunk_causal_attn_fwd_i8qk": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp]),
+    "wf_quant_rows_i8": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "wf_gemm_w8a8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "wf_status_str": (ctypes.c_char_p, [_c_int]),
     "wf_last_error": (ctypes.c_char_p, []),
     "wf_version": (_c_int, []),
@@ -288,3 +291,36 @@ def chunk_causal_attn_fwd_i8qk(q: torch.Tensor, cache: KVCache, n_inflight: int,
                                                _vp(_stream(stream))),
            "wf_chunk_causal_attn_fwd_i8qk")
     return out, lse
+
+
+def quant_rows_i8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Per-row int8 quantization of x [rows][cols] bf16. Returns (codes int8, scales fp32)."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.int8, device=x.device) if codes is None else codes
+    scales = torch.empty(rows, dtype=torch.float32, device=x.device) if scales is None else scales
+    if codes.shape != (rows, cols) or codes.dtype != torch.int8 or scales.shape != (rows,):
+        raise ValueError("codes / scales do not match x")
+    _check(lib().wf_quant_rows_i8(_dev(x, "x"), rows, cols, WF_BF16, _dev(codes, "codes"), _dev(scales, "scales"),
+                                  _vp(_stream(stream))), "wf_quant_rows_i8")
+    return codes, scales
+
+
+def gemm_w8a8(xq: torch.Tensor, sx: Optional[torch.Tensor], wq: torch.Tensor, sw: Optional[torch.Tensor],
+              bias: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """W8A8 linear: y[m][n] = s_x[m] s_w[n] sum_k xq[m,k] wq[n,k] + bias[n] (bf16), or the raw
+    int32 accumulators with out_dtype=torch.int32."""
+    if xq.dtype != torch.int8 or wq.dtype != torch.int8 or xq.dim() != 2 or wq.dim() != 2 or xq.shape[1] != wq.shape[1]:
+        raise ValueError("xq [M][K] and wq [N][K] must be int8 with the same K")
+    M, K = xq.shape
+    N = wq.shape[0]
+    code = {torch.bfloat16: WF_BF16, torch.int32: WF_I32}[out_dtype]
+    out = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    _check(lib().wf_gemm_w8a8(_dev(xq, "xq"), _dev(sx, "sx") if sx is not None else None, _dev(wq, "wq"),
+                              _dev(sw, "sw") if sw is not None else None,
+                              _dev(bias, "bias") if bias is not None else None, M, N, K, code, _dev(out, "out"),
+                              _vp(_stream(stream))), "wf_gemm_w8a8")
+    return out

@@ -324,6 +324,40 @@ WF_EXPORT int wf_chunk_causal_attn_fwd_i8qk(const void* q, const wf_kv_cache* kv
   return hip_status(launch_attn_fwd_i8qk(*kv, p, workspace, static_cast<hipStream_t>(stream)), who);
 }
 
+WF_EXPORT int wf_quant_rows_i8(const void* x, int rows, int cols, int dtype, void* codes, float* scales,
+                               void* stream) {
+  const char* who = "wf_quant_rows_i8";
+  if (!x || !codes || !scales) return fail(WF_E_NULL, "%s: NULL argument", who);
+  if (dtype != WF_BF16) return fail(WF_E_DTYPE, "%s: input must be WF_BF16", who);
+  if (rows < 0 || rows > (1 << 24) || cols < 8 || cols % 8)
+    return fail(WF_E_SHAPE, "%s: need rows in [0, 2^24] and cols a positive multiple of 8 (rows %d cols %d)", who, rows,
+                cols);
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+    return fail(WF_E_SHAPE, "%s: x must be 16-byte, codes 8-byte, scales 4-byte aligned", who);
+  if (rows == 0) return ok();
+  return hip_status(launch_quant_rows_i8(x, rows, cols, codes, scales, static_cast<hipStream_t>(stream)), who);
+}
+
+WF_EXPORT int wf_gemm_w8a8(const void* xq, const float* sx, const void* wq, const float* sw, const void* bias, int M,
+                           int N, int K, int out_dtype, void* y, void* stream) {
+  const char* who = "wf_gemm_w8a8";
+  if (!xq || !wq || !y) return fail(WF_E_NULL, "%s: NULL argument", who);
+  if (out_dtype != WF_BF16 && out_dtype != WF_I32) return fail(WF_E_DTYPE, "%s: out_dtype must be WF_BF16 or WF_I32", who);
+  if (out_dtype == WF_BF16 && (!sx || !sw)) return fail(WF_E_NULL, "%s: NULL scales", who);
+  if (M < 0 || N < 8 || N % 8 || K < 64 || K % 64 || K > 131072)
+    return fail(WF_E_SHAPE, "%s: need N a positive multiple of 8, K a multiple of 64 in [64, 131072] (M %d N %d K %d)",
+                who, M, N, K);
+  // one workgroup per 256 x 256 output tile; the grid stays below 2^22 workgroups
+  if ((size_t)((M + 255) / 256) * (size_t)((N + 255) / 256) > ((size_t)1 << 22))
+    return fail(WF_E_SHAPE, "%s: M x N too large (more than 2^22 tiles of 256 x 256)", who);
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(y, 16) || (sx && !aligned(sx, 4)) || (sw && !aligned(sw, 4)) ||
+      (bias && !aligned(bias, 2)))
+    return fail(WF_E_SHAPE, "%s: xq, wq, y must be 16-byte aligned", who);
+  if (M == 0) return ok();
+  return hip_status(launch_gemm_w8a8(xq, sx, wq, sw, bias, M, N, K, out_dtype == WF_I32, y,
+                                     static_cast<hipStream_t>(stream)), who);
+}
+
 WF_EXPORT const char* wf_status_str(int status) {
   switch (status) {
     case WF_OK: return "WF_OK";

@@ -95,6 +95,11 @@ struct AttnParams {
 
 hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& prm, hipStream_t s);
 
+// ---- W8A8 linear ----
+hipError_t launch_quant_rows_i8(const void* x, int rows, int cols, void* q, float* scales, hipStream_t s);
+hipError_t launch_gemm_w8a8(const void* xq, const float* sx, const void* wq, const float* sw, const void* bias, int M,
+                            int N, int K, bool out_i32, void* y, hipStream_t s);
+
 // ---- int8-QK path ----
 struct I8Layout {
   size_t q_codes, q_scales, k_codes, k_scales, mean, qm, partial, total;

@@ -51,6 +51,7 @@ extern "C" {
 /* ---- element types ---- */
 #define WF_F32 0
 #define WF_BF16 1
+#define WF_I32 2 /* raw int32 accumulators (wf_gemm_w8a8 output only) */
 
 /* Largest number of table entries (history + in-flight chunks) and slots. */
 #define WF_MAX_TABLE 64
@@ -217,6 +218,35 @@ size_t wf_attn_i8qk_workspace_bytes(const wf_kv_cache* kv, int n_inflight);
 int wf_chunk_causal_attn_fwd_i8qk(const void* q, const wf_kv_cache* kv, int n_inflight,
                                   float scale, void* workspace, void* out, float* lse,
                                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * W8A8 linear (the int8 linears around attention). The pages name a W8A8
+ * backend for the DiT linears in their DiT-only tests (Abstract) without its
+ * internals; this is one concrete scheme:
+ *   per row (token of X, output channel of W): s = amax/127 (1 if amax = 0),
+ *   code = clamp(round_half_even(x/s), -127, 127), all decisions in fp32;
+ *   acc[m][n] = sum_k Xq[m][k] Wq[n][k] exactly in int32;
+ *   y[m][n] = bf16( fma((float)acc, s_x[m] * s_w[n], bias[n]) ).
+ * ------------------------------------------------------------------------ */
+
+/* Quantizes rows x[rows][cols] (WF_BF16, device, 16-byte aligned; cols a
+ * multiple of 8; rows <= 2^24) into caller-owned codes int8 [rows][cols]
+ * (8-byte aligned) and scales fp32 [rows], enqueued on the stream.
+ * Errors: WF_E_NULL, WF_E_DTYPE (x not WF_BF16), WF_E_SHAPE (sizes or
+ * alignment), WF_E_HIP (launch); nothing is enqueued on an argument error. */
+int wf_quant_rows_i8(const void* x, int rows, int cols, int dtype, void* codes, float* scales, void* stream);
+
+/* Y = W8A8 linear of xq int8 [M][K] (scales sx [M]) with wq int8 [N][K]
+ * (output features x input features, scales sw [N]) and optional bias
+ * (WF_BF16 [N], may be NULL). out_dtype WF_BF16 gives y bf16 [M][N];
+ * WF_I32 gives the raw int32 accumulators (sx, sw, bias ignored).
+ * Requires N a multiple of 8, K a multiple of 64 (<= 131072, so |acc| < 2^31),
+ * at most 2^22 output tiles of 256 x 256, xq, wq, y 16-byte aligned. All
+ * pointers are caller-owned device pointers; y is written, nothing else.
+ * Errors: WF_E_NULL (xq, wq, y, or sx/sw for WF_BF16 output), WF_E_DTYPE,
+ * WF_E_SHAPE, WF_E_HIP; M = 0 is a no-op. */
+int wf_gemm_w8a8(const void* xq, const float* sx, const void* wq, const float* sw, const void* bias, int M, int N,
+                 int K, int out_dtype, void* y, void* stream);
 
 /* ---- diagnostics ---- */
 const char* wf_status_str(int status); /* static string for a status code      */

@@ -54,7 +54,7 @@ def test_exports_match_header(L):
     declared = wf.header_symbols()
     exported = wf.exported_symbols()
     assert declared == exported, (sorted(set(declared) - set(exported)), sorted(set(exported) - set(declared)))
-    assert len(declared) == 18
+    assert len(declared) == 20
 
 
 def test_version_and_status_strings(L):
@@ -207,6 +207,32 @@ def test_fused_rope_write_argument_errors(L):
     assert L.wf_kv_refresh_rope(h, 0, k, k, 0, None) == WF_E_SLOT  # empty table
     assert table(L, h) == [] and slot.value == -1
     L.wf_kv_cache_destroy(h)
+
+
+def test_w8a8_argument_errors(L):
+    """Row quantization and the W8A8 GEMM refuse bad arguments before any launch; zero rows are a no-op."""
+    p = HostPools()
+    a = ctypes.c_void_p(p.k.value)
+    f = ctypes.cast(ctypes.c_void_p(p.v.value), ctypes.POINTER(ctypes.c_float))
+    q = L.wf_quant_rows_i8
+    assert q(None, 4, 64, wf.WF_BF16, a, f, None) == WF_E_NULL
+    assert q(a, 4, 64, wf.WF_BF16, a, None, None) == WF_E_NULL
+    assert q(a, 4, 64, wf.WF_F32, a, f, None) == WF_E_DTYPE
+    assert q(a, 4, 60, wf.WF_BF16, a, f, None) == WF_E_SHAPE  # cols not a multiple of 8
+    assert q(a, -1, 64, wf.WF_BF16, a, f, None) == WF_E_SHAPE
+    assert q(a, (1 << 24) + 1, 64, wf.WF_BF16, a, f, None) == WF_E_SHAPE
+    assert q(ctypes.c_void_p(a.value + 8), 4, 64, wf.WF_BF16, a, f, None) == WF_E_SHAPE  # misaligned x
+    assert q(a, 0, 64, wf.WF_BF16, a, f, None) == WF_OK
+    g = L.wf_gemm_w8a8
+    assert g(None, f, a, f, None, 4, 8, 64, wf.WF_BF16, a, None) == WF_E_NULL
+    assert g(a, None, a, f, None, 4, 8, 64, wf.WF_BF16, a, None) == WF_E_NULL  # bf16 output needs scales
+    assert g(a, f, a, f, None, 4, 8, 64, wf.WF_F32, a, None) == WF_E_DTYPE
+    assert g(a, f, a, f, None, 4, 12, 64, wf.WF_BF16, a, None) == WF_E_SHAPE  # N % 8
+    assert g(a, f, a, f, None, 4, 8, 96, wf.WF_BF16, a, None) == WF_E_SHAPE   # K % 64
+    assert g(a, f, a, f, None, 4, 8, 131072 + 64, wf.WF_BF16, a, None) == WF_E_SHAPE  # int32 range
+    assert g(a, f, a, f, None, 1 << 30, 1 << 20, 64, wf.WF_BF16, a, None) == WF_E_SHAPE  # grid size
+    assert g(ctypes.c_void_p(a.value + 4), f, a, f, None, 4, 8, 64, wf.WF_BF16, a, None) == WF_E_SHAPE
+    assert g(a, None, a, None, None, 0, 8, 64, wf.WF_I32, a, None) == WF_OK
 
 
 def test_no_gpu_launch_fails_cleanly(L):

@@ -36,6 +36,7 @@ __all__ = [
     "make_stale_refresh",
     "sample_rows",
     "slot_permutation",
+    "make_linear_inputs",
 ]
 
 
@@ -184,6 +185,16 @@ def make_rollout_round(cfg: RoundConfig, r: int):
     rng = np.random.default_rng(400 + r)
     shape = (cfg.nq, cfg.n_heads, cfg.head_dim)
     return tuple(_normal(rng, shape, cfg.dtype) for _ in range(3))
+
+
+def make_linear_inputs(M: int, N: int, K: int, seed: int, w_scale: float = 0.02):
+    """Inputs of one linear layer (bf16-representable float32): X [M][K] ~ N(0,1),
+    W [N][K] ~ N(0, w_scale^2), bias [N] ~ N(0, 0.1^2). Draw order: X, W, bias."""
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (M, K), "bf16")
+    w = _normal(rng, (N, K), "bf16", w_scale)
+    b = _normal(rng, (N,), "bf16", 0.1)
+    return x, w, b
 
 
 def slot_permutation(n_slots: int, seed: int) -> List[int]:
