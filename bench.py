@@ -15,9 +15,10 @@ Prints ONE JSON line. value = effective attention FLOPs per round / step time
 head (padding, skipped tiles and softmax not counted). Also reported: the
 attention kernel alone against the bf16 MFMA peak (roofline, timed with
 events on the stream it runs on), chunk-rounds/s, the cache writes against
-HBM bandwidth and, unless --no-extras, the long-rollout round with 3D RoPE
-and the 14B-shaped int8-QK round; and the fp64 oracle timed on the host on a
-bounded sample of the same round.
+HBM bandwidth and, unless --no-extras, the long-rollout round with 3D RoPE,
+the 14B-shaped int8-QK round and the W8A8 linears around attention (QKV and
+O projections of the round's tokens); and the fp64 oracle timed on the host
+on a bounded sample of the same round.
 """
 from __future__ import annotations
 
@@ -312,6 +313,72 @@ def bench_i8qk(torch, wf, cfg, steps, warmup, stream):
     }
 
 
+# Linear shapes of the DiT blocks around attention: (name, out features, in features).
+W8A8_SHAPES = [
+    ("wan13b_qkv", 4608, 1536), ("wan13b_o", 1536, 1536),
+    ("wan14b_qkv", 15360, 5120), ("wan14b_o", 5120, 5120),
+]
+
+
+def bench_w8a8(torch, wf, tokens, steps, warmup, stream):
+    """W8A8 linears on one round's in-flight tokens: per-token activation quantization and the
+    int8 GEMM with the scale/bias epilogue, per shape; hipBLASLt's int8 GEMM (int32 output, no
+    epilogue) timed beside it as context."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8)
+    out = {"tokens": tokens, "data": "X ~ N(0,1), W ~ N(0, 0.02^2), bias ~ N(0, 0.1^2), bf16, device RNG"}
+    for name, N, K in W8A8_SHAPES:
+        x = torch.randn(tokens, K, generator=g, device="cuda").to(torch.bfloat16)
+        w = (torch.randn(N, K, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        b = (torch.randn(N, generator=g, device="cuda") * 0.1).to(torch.bfloat16)
+        wq, sw = wf.quant_rows_i8(w)
+        xq, sx = wf.quant_rows_i8(x)
+        y = wf.gemm_w8a8(xq, sx, wq, sw, b)
+        for _ in range(warmup):
+            wf.quant_rows_i8(x, xq, sx)
+            wf.gemm_w8a8(xq, sx, wq, sw, b, out=y)
+        timers = [Timer(torch, stream, 3) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for t in timers:
+            t.mark(0)
+            wf.quant_rows_i8(x, xq, sx)
+            t.mark(1)
+            wf.gemm_w8a8(xq, sx, wq, sw, b, out=y)
+            t.mark(2)
+        torch.cuda.synchronize()
+        q_ms = np.array([t.ms(0, 1) for t in timers])
+        g_ms = np.array([t.ms(1, 2) for t in timers])
+        ops = 2.0 * tokens * N * K
+        tops = ops / (np.median(g_ms) / 1e3) / 1e12
+        qbytes = tokens * K * 3 + tokens * 4  # bf16 in, int8 codes and fp32 scales out
+        ref = {}
+        try:
+            wt = wq.t()
+            for _ in range(3):
+                torch._int_mm(xq, wt)
+            tl = [Timer(torch, stream, 2) for _ in range(steps)]
+            torch.cuda.synchronize()
+            for t in tl:
+                t.mark(0)
+                torch._int_mm(xq, wt)
+                t.mark(1)
+            torch.cuda.synchronize()
+            r_ms = np.array([t.ms(0, 1) for t in tl])
+            ref = {"hipblaslt_int8_gemm_ms_median": pct(r_ms, 50),
+                   "hipblaslt_tops_median": ops / (np.median(r_ms) / 1e3) / 1e12}
+        except Exception as e:  # context only
+            ref = {"hipblaslt_int8_gemm": f"unavailable: {type(e).__name__}"}
+        out[name] = {
+            "M_N_K": [tokens, N, K],
+            "gemm": {**ms_summary(g_ms), "tops_median": tops, "frac_of_int8_peak": tops / INT8_DENSE_TOPS},
+            "quant_activations": {**ms_summary(q_ms), "gbs_median": qbytes / (np.median(q_ms) / 1e3) / 1e9},
+            **ref,
+        }
+        del x, w, b, wq, sw, xq, sx, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_power(torch, wf, cfg, seconds):
     """Board power while the headline attention runs back to back, and energy per launch."""
     from chunk_causal_dit_amd.profiling import sample_power
@@ -361,8 +428,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=4680, help="query rows per chunk in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the rollout and int8-QK measurements")
+    ap.add_argument("--no-extras", action="store_true", help="skip the rollout, int8-QK and W8A8 measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0, help="run a plain copy of this size first")
+    ap.add_argument("--w8a8-only", action="store_true",
+                    help="run only the W8A8 linear measurement and print its JSON (for profiling)")
     ap.add_argument("--power-seconds", type=float, default=3.0,
                     help="seconds of back-to-back attention launches with the board power sensor read (0: off)")
     args = ap.parse_args()
@@ -387,6 +456,9 @@ def main():
         copy_probe(torch, args.copy_probe_mib)
 
     cfg = CONFIGS["wan13b_4step"]
+    if args.w8a8_only:
+        print(json.dumps({"w8a8": bench_w8a8(torch, wf, cfg.nq, args.steps, args.warmup, stream)}), flush=True)
+        return
     inp, ms_per_step, kv_ms, attn_ms = bench_round(torch, wf, cfg, args.steps, args.warmup, stream)
     print(f"[bench] {cfg.name}: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
@@ -448,6 +520,8 @@ def main():
         torch.cuda.empty_cache()
         res["i8qk"] = bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], 20, 3, stream)
         print("[bench] int8-QK done", file=sys.stderr, flush=True)
+        res["w8a8"] = bench_w8a8(torch, wf, cfg.nq, 20, 3, stream)
+        print("[bench] W8A8 linears done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
     print(json.dumps(res), flush=True)

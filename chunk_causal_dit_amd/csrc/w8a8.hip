@@ -6,20 +6,26 @@
 //
 // GEMM: Y[M][N] = s_x[m] s_w[n] sum_k Xq[m][k] Wq[n][k] (+ bias[n]),
 // X and W both row-major with K contiguous.
-//   * workgroup tile 256 x 256, 8 waves of 64 x 128 (2 x 4 MFMA tiles of
-//     32 x 32), v_mfma_i32_32x32x32_i8;
+//   * workgroup tile 256 x 256, 4 waves of 128 x 128 (4 x 4 MFMA tiles of
+//     32 x 32), v_mfma_i32_32x32x32_i8, one wave per SIMD: the large wave
+//     tile keeps LDS reads at 64 B/clk per CU at full MFMA rate (LDS serves
+//     about 128 B/clk, and the HBM -> LDS copies take another 32);
 //   * K advances 64 bytes per stage; three LDS stages of A and B (32 KB
-//     each) filled by direct HBM -> LDS copies (global_load_lds_dwordx4)
-//     two stages ahead;
+//     each) filled by direct HBM -> LDS copies (global_load_lds_dwordx4);
+//     the operands of the next k32 step are read into a second register set
+//     while the MFMAs of the current one run, and the one barrier per stage
+//     sits between the two k32 steps, where the stage's buffer is free to refill;
 //   * LDS tile rows are 64 bytes (four 16-byte pieces); piece p of row r sits
 //     in slot p ^ ((r >> 2) & 3), so the 16 lanes of an MFMA operand read hit
 //     16 different bank groups while each copy instruction still reads whole
 //     64-byte row segments from HBM;
 //   * epilogue in fp32: (float)acc * (s_x[m] * s_w[n]) + bias[n], rounded to
 //     bf16, staged through LDS and stored as full 16-byte row pieces;
-//   * XCD-contiguous tile order: each XCD gets one contiguous run of the
-//     column-major tile order, i.e. a few weight tiles that stay in its L2.
+//   * XCD-aware tile order: each XCD gets one contiguous run of a banded
+//     order (4 tile rows at a time), so the tiles it runs together share
+//     operands in its L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "wf_internal.h"
 
@@ -68,165 +74,230 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const __bf16* __restric
 
 // ---------------------------------------------------------------- GEMM
 constexpr int BM = 256, BN = 256, BK = 64;  // BK in bytes (= int8 elements)
-constexpr int NWV = 8;                      // waves: 4 along M x 2 along N
+constexpr int NWV = 4;                      // waves: 2 along M x 2 along N, 128 x 128 each
 constexpr int NST = 3;                      // LDS stages
 constexpr int TILE_A = BM * BK, TILE_B = BN * BK;
-constexpr int STAGE = TILE_A + TILE_B;
-constexpr int LDS_MAIN = NST * STAGE;                 // 96 KB
-constexpr int LDS_OUT = BM * BN * 2;                  // bf16 output staging, 128 KB
+constexpr int STAGE = TILE_A + TILE_B;      // 32 KB
+constexpr int LDS_MAIN = NST * STAGE;
+constexpr int OUT_LD = BN + 8;              // bf16 staging row stride (elements); 528 bytes
+constexpr int LDS_OUT = BM * OUT_LD * 2;
 constexpr int LDS_BYTES = LDS_OUT > LDS_MAIN ? LDS_OUT : LDS_MAIN;
+constexpr int COPIES = 2 * (BM / 16) / NWV;  // copy instructions per wave per stage (A and B)
+static_assert(BM == BN, "copy_rows serves both operands");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
 extern __shared__ __attribute__((aligned(1024))) char g_lds[];
 
 __device__ __forceinline__ int slot_of(int r, int p) { return p ^ ((r >> 2) & 3); }
 
 // Copies the 64-byte K slice [k0, k0+64) of 256 consecutive rows (row0 ..) of a
-// row-major int8 matrix into an LDS tile image: wave w issues instructions w
-// and w + 8 of 16; instruction j covers rows 16j .. 16j+15, lane i the piece
-// (i % 4) ^ ((row >> 2) & 3) of row 16j + i / 4. Rows past `rows` repeat the last row.
+// row-major int8 matrix into an LDS tile image: instruction j (0..15) covers
+// rows 16j .. 16j+15, lane i the piece (i % 4) ^ ((row >> 2) & 3) of row
+// 16j + i / 4; wave w issues instructions w, w+4, w+8, w+12. Rows past `rows`
+// repeat the last row.
+__device__ __forceinline__ void copy_row_piece(const signed char* src, int rows, int row0, int K, int k0, char* lds,
+                                               int wave, int lane, int u) {
+  const int j = wave + u * NWV;
+  const int r = 16 * j + (lane >> 2);
+  const int p = slot_of(r, lane & 3);
+  const int gr = min(row0 + r, rows - 1);
+  __builtin_amdgcn_global_load_lds(src + (size_t)gr * K + k0 + p * 16, (LDS_AS void*)(lds + j * 1024), 16, 0, 0);
+}
 __device__ __forceinline__ void copy_rows(const signed char* src, int rows, int row0, int K, int k0, char* lds,
                                           int wave, int lane) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int j = wave + u * NWV;
-    const int r = 16 * j + (lane >> 2);
-    const int p = slot_of(r, lane & 3);
-    const int gr = min(row0 + r, rows - 1);
-    __builtin_amdgcn_global_load_lds(src + (size_t)gr * K + k0 + p * 16, (LDS_AS void*)(lds + j * 1024), 16, 0, 0);
-  }
+  for (int u = 0; u < BM / 16 / NWV; ++u) copy_row_piece(src, rows, row0, K, k0, lds, wave, lane, u);
 }
 
-#define WF_W8_WAIT_VM_BARRIER(n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+// Waits until at most N copy instructions of this wave are in flight and all
+// its LDS reads are done, then joins the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0, "unsupported wait count");
+}
 
-// XCD-contiguous order: workgroup b runs on XCD b % 8; XCD x takes the x-th
-// contiguous run of the column-major tile order (tile row fastest).
-__device__ __forceinline__ void tile_of(int b, int tm_count, int total, int& tm, int& tn) {
+// Tile order: workgroup b runs on XCD b % 8, and XCD x takes the x-th contiguous
+// run of the order. The order walks bands of 4 tile rows, column by column inside
+// a band, so the 32 workgroups an XCD runs at once share 4 X tiles and about 8 W
+// tiles in its L2, and a band's X rows stay there while its columns pass.
+__device__ __forceinline__ void tile_of(int b, int tm_count, int tn_count, int& tm, int& tn) {
+  constexpr int G = 4;
+  const int total = tm_count * tn_count;
   const int q = total / 8, rem = total % 8;
   const int x = b % 8, i = b / 8;
   const int item = x * q + min(x, rem) + i;
-  tm = item % tm_count;
-  tn = item / tm_count;
+  const int band = item / (G * tn_count), in = item % (G * tn_count);
+  const int rows = min(G, tm_count - band * G);
+  tm = band * G + in % rows;
+  tn = in / rows;
 }
 
 template <bool OUT_I32>
-__global__ __launch_bounds__(NWV * 64) void gemm_w8a8_kernel(const signed char* __restrict__ xq,
-                                                             const float* __restrict__ sx,
-                                                             const signed char* __restrict__ wq,
-                                                             const float* __restrict__ sw,
-                                                             const __bf16* __restrict__ bias, int M, int N, int K,
-                                                             void* __restrict__ y) {
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w8a8_kernel(
+    const signed char* __restrict__ xq, const float* __restrict__ sx, const signed char* __restrict__ wq,
+    const float* __restrict__ sw, const __bf16* __restrict__ bias, int M, int N, int K, void* __restrict__ y) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_m * tiles_n, tm, tn);
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 3, wn = wave >> 2;  // wave tile: rows wm*64 .. +64, cols wn*128 .. +128
+  const int wm = wave & 1, wn = wave >> 1;  // wave tile: rows wm*128 .. +128, cols wn*128 .. +128
   const int rr = lane & 31, hh = lane >> 5;
   char* lds = g_lds;
-  auto stA = [&](int s) { return lds + s * STAGE; };
-  auto stB = [&](int s) { return lds + s * STAGE + TILE_A; };
   const int KT = K / BK;
 
   auto copy_stage = [&](int kt, int s) {
-    copy_rows(xq, M, m0, K, kt * BK, stA(s), wave, lane);
-    copy_rows(wq, N, n0, K, kt * BK, stB(s), wave, lane);
+    copy_rows(xq, M, m0, K, kt * BK, lds + s * STAGE, wave, lane);
+    copy_rows(wq, N, n0, K, kt * BK, lds + s * STAGE + TILE_A, wave, lane);
   };
-  copy_stage(0, 0);
-  if (KT > 1) copy_stage(1, 1);
-  WF_W8_WAIT_VM_BARRIER(0);
 
-  i32x16 acc[2][4];
+  // Operand rows of this lane: A row wm*128 + 32i + rr, B row wn*128 + 32j + rr. In k32 step
+  // ks of a stage the lane takes piece 2ks + hh, stored in slot (2ks + hh) ^ ((rr >> 2) & 3);
+  // block i (j) adds 32 rows = 2048 bytes.
+  const int x = (rr >> 2) & 3;
+  int aoff[2], boff[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int ks = 0; ks < 2; ++ks) {
+    aoff[ks] = (wm * 128 + rr) * 64 + 16 * ((2 * ks + hh) ^ x);
+    boff[ks] = TILE_A + (wn * 128 + rr) * 64 + 16 * ((2 * ks + hh) ^ x);
+  }
+  i32x4 a0[4], b0[4], a1[4], b1[4];
+  auto load_ops = [&](const char* st, int ks, i32x4(&av)[4], i32x4(&bv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const i32x4*>(st + aoff[ks] + 2048 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = *reinterpret_cast<const i32x4*>(st + boff[ks] + 2048 * j);
+  };
+  // acc[i][j]: D = Bblock_j x Ablock_i^T, so lane l holds m = 32i + (l % 32) and four runs of
+  // four consecutive n: n = 32j + 8g + 4hh + (0..3) in elements 4g .. 4g+3
+  i32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+  auto mma = [&](const i32x4(&av)[4], const i32x4(&bv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv[j], av[i], acc[i][j], 0, 0, 0);
+  };
 
-  // per-lane LDS offsets of the operand rows (row index fixed per lane; the piece varies)
-  int aoff[2][4], boff[4][4];  // [block][piece]
+  // prologue: every stage buffer in flight; wait for stage 0
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = wm * 64 + 32 * i + rr;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) aoff[i][p] = r * 64 + 16 * slot_of(r, p);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = wn * 128 + 32 * j + rr;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) boff[j][p] = r * 64 + 16 * slot_of(r, p);
-  }
+  for (int st = 0; st < NST; ++st)
+    if (st < KT) copy_stage(st, st);
+  if (KT >= NST) wait_vm_barrier<COPIES * (NST - 1)>();
+  else wait_vm_barrier<0>();
+  load_ops(lds, 0, a0, b0);
 
-  for (int kt = 0, s = 0; kt < KT; ++kt, s = s == NST - 1 ? 0 : s + 1) {
-    const char* a = stA(s);
-    const char* b = stB(s);
+  // One stage: reads of its second k32 step under the MFMAs of the first; then the barrier
+  // (stage kt+1 has landed, every wave's reads of stage kt are done), the refill of the
+  // buffer just read, and the reads of the next stage's first step under the second MFMAs.
+  // The steady-state body has no branches, so the compiler's own waits before the MFMAs
+  // count only the reads each MFMA needs.
+  // Instruction order inside each half is pinned: MFMAs alternate with the reads (and
+  // copies), so the matrix pipe never waits behind a run of memory instructions.
+  auto body = [&](auto full, int kt, int s) {
+    const int s1 = s == NST - 1 ? 0 : s + 1;
+    __builtin_amdgcn_sched_barrier(0);
+    load_ops(lds + s * STAGE, 1, a1, b1);
+    mma(a0, b0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {  // two k32 steps per stage
-      const int p = 2 * ks + hh;
-      i32x4 av[2], bv[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = *reinterpret_cast<const i32x4*>(a + aoff[i][p]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = *reinterpret_cast<const i32x4*>(b + boff[j][p]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[i], bv[j], acc[i][j], 0, 0, 0);
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
-    // copies of stage kt+2 into the stage read in step kt-1, then wait for stage kt+1
-    if (kt + 2 < KT) {
-      const int s2 = s == 0 ? 2 : s - 1;
-      copy_stage(kt + 2, s2);
-      WF_W8_WAIT_VM_BARRIER(4);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(full)::value) {
+      wait_vm_barrier<COPIES * (NST - 2)>();
+      __builtin_amdgcn_sched_barrier(0);
+      // one MFMA per slot; after it the next stage's operand reads (needed first), then
+      // the copies that refill this stage's buffer with stage kt + NST
+      const char* nst = lds + s1 * STAGE;
+      char* cst = lds + s * STAGE;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int i = t >> 2, j = t & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[j], a1[i], acc[i][j], 0, 0, 0);
+        if (t < 4) a0[t] = *reinterpret_cast<const i32x4*>(nst + aoff[0] + 2048 * t);
+        else if (t < 8) b0[t - 4] = *reinterpret_cast<const i32x4*>(nst + boff[0] + 2048 * (t - 4));
+        else if (t < 12) copy_row_piece(xq, M, m0, K, (kt + NST) * BK, cst, wave, lane, t - 8);
+        else copy_row_piece(wq, N, n0, K, (kt + NST) * BK, cst + TILE_A, wave, lane, t - 12);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
-      WF_W8_WAIT_VM_BARRIER(0);
+      wait_vm_barrier<0>();
+      if (kt + 1 < KT) load_ops(lds + s1 * STAGE, 0, a0, b0);
+      mma(a1, b1);
     }
-  }
+  };
+  int kt = 0, s = 0;
+  for (; kt + NST < KT; ++kt, s = s == NST - 1 ? 0 : s + 1) body(std::true_type{}, kt, s);
+  for (; kt < KT; ++kt, s = s == NST - 1 ? 0 : s + 1) body(std::false_type{}, kt, s);
+  __syncthreads();
 
-  // accumulator element e of lane l in tile (i, j): row 8*(e/4) + 4*hh + e%4, column rr
   if constexpr (OUT_I32) {
     int* yo = static_cast<int*>(y);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 128 + 32 * i + rr;
+      if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 128 + 32 * j + rr;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3);
-          if (m < M && n < N) yo[(size_t)m * N + n] = acc[i][j][e];
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * 128 + 32 * j + 8 * g + 4 * hh;
+          if (n < N)
+            *reinterpret_cast<i32x4*>(yo + (size_t)m * N + n) =
+                i32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         }
-      }
+    }
     return;
   }
-  // fp32 epilogue into the bf16 LDS staging tile [BM][BN] (the stages are no longer read)
+  // fp32 epilogue into the bf16 staging tile [BM][OUT_LD] (the stages are no longer read)
   __bf16* out_lds = reinterpret_cast<__bf16*>(lds);
+  float sxm[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int cl = wn * 128 + 32 * j + rr;
-    const int n = min(n0 + cl, N - 1);
-    const float swn = sw[n];
-    const float bn = bias ? (float)bias[n] : 0.f;
+  for (int i = 0; i < 4; ++i) sxm[i] = sx[min(m0 + wm * 128 + 32 * i + rr, M - 1)];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rl = wm * 64 + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const float sxm = sx[min(m0 + rl, M - 1)];
-        out_lds[rl * BN + cl] = (__bf16)fmaf((float)acc[i][j][e], sxm * swn, bn);
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn * 128 + 32 * j + 8 * g + 4 * hh;
+      float swn[4], bn[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = min(n0 + nl + c, N - 1);
+        swn[c] = sw[n];
+        bn[c] = bias ? (float)bias[n] : 0.f;
       }
-  }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ml = wm * 128 + 32 * i + rr;
+        __bf16 v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = (__bf16)fmaf((float)acc[i][j][4 * g + c], sxm[i] * swn[c], bn[c]);
+        *reinterpret_cast<uint2*>(out_lds + ml * OUT_LD + nl) = *reinterpret_cast<const uint2*>(v);
+      }
+    }
   __syncthreads();
   // coalesced stores: 16-byte pieces (8 columns) of each row
   __bf16* yo = static_cast<__bf16*>(y);
   constexpr int PIECES = BM * BN / 8;
+#pragma unroll 4
   for (int idx = tid; idx < PIECES; idx += NWV * 64) {
     const int rl = idx / (BN / 8), cp = idx % (BN / 8);
     const int m = m0 + rl, n = n0 + cp * 8;
     if (m < M && n < N)
-      *reinterpret_cast<u32x4*>(yo + (size_t)m * N + n) = *reinterpret_cast<const u32x4*>(out_lds + rl * BN + cp * 8);
+      *reinterpret_cast<u32x4*>(yo + (size_t)m * N + n) = *reinterpret_cast<const u32x4*>(out_lds + rl * OUT_LD + cp * 8);
   }
 }
 
