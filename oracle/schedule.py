@@ -68,7 +68,7 @@ def round_plan(n_steps: int, n_chunks: int, hist_window: int, r: int) -> Dict:
         if 0 <= s <= S and not (c == F - 1 and s == S):
             inflight.append((c, s))
     refreshed_before = [c for c in range(F) if c + S < r and c != F - 1]
-    hist = refreshed_before[len(refreshed_before) - hist_window:] if hist_window > 0 else []
+    hist = refreshed_before[-hist_window:] if hist_window > 0 else []  # all of them when fewer than W
     output = None
     for c, s in inflight:
         if s == S - 1:

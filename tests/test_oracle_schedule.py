@@ -114,7 +114,8 @@ def test_rollout_attention_matches_scalar_assembly():
                     assert abs(lse[h, qi * C + t] - (m + math.log(z))) < 1e-12
 
 
-@pytest.mark.parametrize("kind", ["noisiest_first", "refresh_late", "window_plus_one", "refresh_chunk_in_history"])
+@pytest.mark.parametrize("kind", ["noisiest_first", "refresh_late", "window_plus_one", "refresh_chunk_in_history",
+                                  "window_slice_wraps"])
 def test_planted_mistakes_are_caught(kind):
     def bad_plan(S, F, W, r):
         p = SC.round_plan(S, F, W, r)
@@ -125,6 +126,9 @@ def test_planted_mistakes_are_caught(kind):
         elif kind == "window_plus_one":
             done = [c for c in range(F) if c + S < r and c != F - 1]
             p["hist"] = done[-(W + 1):]
+        elif kind == "window_slice_wraps":  # slice start len - W goes negative while fewer than W are done
+            done = [c for c in range(F) if c + S < r and c != F - 1]
+            p["hist"] = done[len(done) - W:] if W > 0 else []
         elif kind == "refresh_chunk_in_history":  # history already holds the chunk refreshed this round
             done = [c for c in range(F) if c + S <= r and c != F - 1]
             p["hist"] = done[-W:]
