@@ -17,7 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-from typing import List, Optional, Sequence, Tuple
+from typing import Callable, List, Optional, Sequence, Tuple
 
 import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 
@@ -26,6 +26,7 @@ __all__ = [
     "WF_F32", "WF_BF16", "KVCache", "kv_pool_bytes", "rope3d",
     "chunk_causal_attn_fwd", "attn_i8qk_workspace_bytes", "chunk_causal_attn_fwd_i8qk",
     "quant_rows_i8", "gemm_w8a8", "WF_I32",
+    "WF_MAX_TABLE", "RoundPlan", "rounds_1f1c", "plan_1f1c", "run_round", "Rollout1F1C",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +34,7 @@ _ROOT = os.path.dirname(_HERE)
 HEADER = os.path.join(_ROOT, "include", "wf.h")
 
 WF_F32, WF_BF16, WF_I32 = 0, 1, 2
+WF_MAX_TABLE = 64
 WF_KV_ADOPT, WF_KV_ZERO_FILL = 0, 1
 _DTYPE = {torch.float32: WF_F32, torch.bfloat16: WF_BF16}
 
@@ -48,6 +50,36 @@ def library_path() -> str:
 
 
 _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+
+class RoundPlan(ctypes.Structure):
+    """One round of a 1F1C rollout (the C struct wf_round_plan)."""
+
+    _fields_ = [
+        ("round", _c_int), ("n_inflight", _c_int),
+        ("inflight_chunk", _c_int * WF_MAX_TABLE), ("inflight_stage", _c_int * WF_MAX_TABLE),
+        ("n_hist", _c_int), ("hist_chunk", _c_int * WF_MAX_TABLE),
+        ("new_chunk", _c_int), ("output_chunk", _c_int), ("evict_after", _c_int),
+    ]
+
+    @property
+    def inflight(self) -> List[Tuple[int, int]]:
+        """(chunk, stage) cleanest first; stage n_steps is the refresh pass."""
+        return [(self.inflight_chunk[i], self.inflight_stage[i]) for i in range(self.n_inflight)]
+
+    @property
+    def hist(self) -> List[int]:
+        return [self.hist_chunk[i] for i in range(self.n_hist)]
+
+    @property
+    def new(self) -> Optional[int]:
+        return None if self.new_chunk < 0 else self.new_chunk
+
+    @property
+    def output(self) -> Optional[int]:
+        return None if self.output_chunk < 0 else self.output_chunk
+
+
 _SIGNATURES = {
     "wf_kv_pool_bytes": (_c_size, [_c_int] * 5),
     "wf_kv_cache_create": (_c_int, [ctypes.POINTER(_vp), _vp, _vp] + [_c_int] * 6 + [_vp]),
@@ -66,6 +98,10 @@ _SIGNATURES = {
     "wf_chunk_causal_attn_fwd_i8qk": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp]),
     "wf_quant_rows_i8": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "wf_gemm_w8a8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "wf_1f1c_rounds": (_c_int, [_c_int, _c_int]),
+    "wf_1f1c_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(RoundPlan)]),
+    "wf_1f1c_run_round": (_c_int, [_vp, ctypes.POINTER(RoundPlan), _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                   ctypes.c_float, _vp, _vp, _vp]),
     "wf_status_str": (ctypes.c_char_p, [_c_int]),
     "wf_last_error": (ctypes.c_char_p, []),
     "wf_version": (_c_int, []),
@@ -324,3 +360,65 @@ def gemm_w8a8(xq: torch.Tensor, sx: Optional[torch.Tensor], wq: torch.Tensor, sw
                               _dev(bias, "bias") if bias is not None else None, M, N, K, code, _dev(out, "out"),
                               _vp(_stream(stream))), "wf_gemm_w8a8")
     return out
+
+
+def rounds_1f1c(n_steps: int, n_chunks: int) -> int:
+    """Rounds of a 1F1C rollout of n_chunks chunks with n_steps denoising steps."""
+    n = lib().wf_1f1c_rounds(n_steps, n_chunks)
+    if n < 0:
+        _check(n, "wf_1f1c_rounds")
+    return n
+
+
+def plan_1f1c(n_steps: int, n_chunks: int, hist_window: int, r: int) -> RoundPlan:
+    """The plan of round r (host only)."""
+    p = RoundPlan()
+    _check(lib().wf_1f1c_plan(n_steps, n_chunks, hist_window, r, ctypes.byref(p)), "wf_1f1c_plan")
+    return p
+
+
+def run_round(cache: KVCache, plan: RoundPlan, q: torch.Tensor, ks: Sequence[torch.Tensor],
+              vs: Sequence[torch.Tensor], scale: float, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None, with_lse: bool = True, stream=None):
+    """One round on the stream: append the new chunk, refresh the other in-flight entries,
+    attention over the round's query block, evict. ks[i], vs[i] are this round's K/V of
+    in-flight chunk i (cleanest first). Returns (out, lse or None)."""
+    N = plan.n_inflight
+    if len(ks) != N or len(vs) != N:
+        raise ValueError(f"need {N} K and V chunks, got {len(ks)} and {len(vs)}")
+    out, lse = _attn_io(q, cache, N, out, lse, with_lse)
+    kp = (_vp * N)(*[cache._chunk(t, "k").value for t in ks])
+    vp = (_vp * N)(*[cache._chunk(t, "v").value for t in vs])
+    _check(lib().wf_1f1c_run_round(cache.handle, ctypes.byref(plan), _dev(q, "q"), kp, vp, float(scale),
+                                   _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
+                                   _vp(_stream(stream))), "wf_1f1c_run_round")
+    return out, lse
+
+
+class Rollout1F1C:
+    """Drives a whole 1F1C rollout of one layer through the library.
+
+    model(plan) returns the round's query block [n_inflight*C][H][D] and the lists of
+    this round's K and V chunks of the in-flight chunks, cleanest first. Each call of
+    step() plans the next round (wf_1f1c_plan) and enqueues it (wf_1f1c_run_round)."""
+
+    def __init__(self, n_steps: int, n_chunks: int, hist_window: int, chunk_tokens: int, n_heads: int,
+                 head_dim: int, scale: float, dtype: torch.dtype = torch.bfloat16, n_slots: Optional[int] = None,
+                 stream=None):
+        self.n_steps, self.n_chunks, self.hist_window, self.scale = n_steps, n_chunks, hist_window, scale
+        self.n_rounds = rounds_1f1c(n_steps, n_chunks)
+        plan_1f1c(n_steps, n_chunks, hist_window, 0)  # validates the window
+        need = hist_window + n_steps + 1
+        self.cache = KVCache(n_slots or need, chunk_tokens, n_heads, head_dim, dtype, stream=stream)
+        self.round = 0
+        self.stream = stream
+
+    def step(self, model: Callable, out: Optional[torch.Tensor] = None, with_lse: bool = False):
+        """Runs the next round. Returns (plan, out, lse or None)."""
+        if self.round >= self.n_rounds:
+            raise StopIteration("the rollout is complete")
+        plan = plan_1f1c(self.n_steps, self.n_chunks, self.hist_window, self.round)
+        q, ks, vs = model(plan)
+        o, l = run_round(self.cache, plan, q, ks, vs, self.scale, out=out, with_lse=with_lse, stream=self.stream)
+        self.round += 1
+        return plan, o, l

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libwf.so")
 
-SOURCES = ["wf_api.cpp", "kv_cache.hip", "rope3d.hip", "attn_fwd.hip", "attn_i8qk.hip", "w8a8.hip"]
+SOURCES = ["wf_api.cpp", "rollout.cpp", "kv_cache.hip", "rope3d.hip", "attn_fwd.hip", "attn_i8qk.hip", "w8a8.hip"]
 ARCH = "gfx950"
 
 

@@ -248,6 +248,58 @@ int wf_quant_rows_i8(const void* x, int rows, int cols, int dtype, void* codes, 
 int wf_gemm_w8a8(const void* xq, const float* sx, const void* wq, const float* sw, const void* bias, int M, int N,
                  int K, int out_dtype, void* y, void* stream);
 
+/* ------------------------------------------------------------------------
+ * 1F1C rollout: the round structure around the attention path.
+ * The pages stagger the denoising stages and the cache-refresh stage so that
+ * they run concurrently, and after the pipeline fills every forward round
+ * outputs one chunk (Abstract); the run holds wp-size = steps + 1 stages
+ * (airadar.tv summaries, usage section). Reading used here:
+ *   stage s of chunk c runs in round c + s; s = 0 .. n_steps-1 are the
+ *   denoising steps (0 = noisiest), s = n_steps is the refresh pass that
+ *   writes the finished chunk's clean K/V for later chunks;
+ *   round r's query block lists its chunks cleanest first (ascending chunk);
+ *   the chunk at stage n_steps-1 is the round's output, so rounds
+ *   0 .. n_steps-2 output nothing (pipeline fill);
+ *   the last chunk has no refresh pass: n_chunks chunks take
+ *   n_chunks + n_steps - 1 rounds;
+ *   history in round r: the newest hist_window chunks whose refresh pass
+ *   ran in an earlier round.
+ * ------------------------------------------------------------------------ */
+typedef struct wf_round_plan {
+  int round;
+  int n_inflight;                   /* chunks in this round's query block, 1 .. n_steps + 1 */
+  int inflight_chunk[WF_MAX_TABLE]; /* their chunk ids, cleanest first                     */
+  int inflight_stage[WF_MAX_TABLE]; /* their stages; n_steps = the refresh pass            */
+  int n_hist;                       /* history chunks visible this round                   */
+  int hist_chunk[WF_MAX_TABLE];     /* their chunk ids, oldest first                       */
+  int new_chunk;                    /* chunk entering at stage 0 (appended), or -1         */
+  int output_chunk;                 /* chunk finishing its last denoising stage, or -1     */
+  int evict_after;                  /* oldest entries to evict after attention             */
+} wf_round_plan;
+
+/* Rounds of a rollout: n_chunks + n_steps - 1, or a negative status for
+ * n_steps < 1, n_chunks < 1 or n_steps + 1 > WF_MAX_TABLE. */
+int wf_1f1c_rounds(int n_steps, int n_chunks);
+
+/* Fills *plan for round `round` (0 .. rounds-1). Needs hist_window >= 0 and
+ * hist_window + n_steps + 1 <= WF_MAX_TABLE. Host only; no device work. */
+int wf_1f1c_plan(int n_steps, int n_chunks, int hist_window, int round, wf_round_plan* plan);
+
+/* Enqueues one round on the stream, in this order: append the new chunk's
+ * K/V (k[n_inflight-1], v[n_inflight-1]) when plan->new_chunk >= 0; refresh
+ * every other in-flight entry i with k[i], v[i] (this round's K/V of that
+ * chunk, [chunk_tokens][n_heads][head_dim] each, 16-byte aligned); run
+ * wf_chunk_causal_attn_fwd over the n_inflight chunks (q, out: the round's
+ * query block [n_inflight*chunk_tokens][n_heads][head_dim]; lse optional);
+ * evict plan->evict_after oldest entries. The cache table must hold the
+ * previous round's state: n_hist + n_inflight entries, less one when a chunk
+ * is appended. k and v are host arrays of n_inflight device pointers.
+ * Every argument is checked before anything is enqueued (WF_E_NULL,
+ * WF_E_SHAPE, WF_E_FULL; the cache is unchanged on these); WF_E_HIP means a
+ * launch was rejected after earlier steps of the round were enqueued. */
+int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, const void* q, const void* const* k,
+                      const void* const* v, float scale, void* out, float* lse, void* stream);
+
 /* ---- diagnostics ---- */
 const char* wf_status_str(int status); /* static string for a status code      */
 const char* wf_last_error(void);      /* thread-local text of the last failure */

@@ -54,7 +54,7 @@ def test_exports_match_header(L):
     declared = wf.header_symbols()
     exported = wf.exported_symbols()
     assert declared == exported, (sorted(set(declared) - set(exported)), sorted(set(exported) - set(declared)))
-    assert len(declared) == 20
+    assert len(declared) == 23
 
 
 def test_version_and_status_strings(L):

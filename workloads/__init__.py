@@ -37,6 +37,7 @@ __all__ = [
     "sample_rows",
     "slot_permutation",
     "make_linear_inputs",
+    "NullModel",
 ]
 
 
@@ -209,3 +210,21 @@ def sample_rows(n_rows: int, n_sample: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     pick = rng.choice(np.arange(1, n_rows - 1), size=n_sample - 2, replace=False)
     return np.sort(np.concatenate([[0, n_rows - 1], pick]))
+
+
+class NullModel:
+    """Stand-in for the DiT in a multi-round rollout: the Q, K, V [C][H][D] that chunk c
+    has at stage s (s = n_steps: the clean chunk of the refresh pass) are seeded draws,
+    rng = default_rng([seed, c, s]), in the order Q, K, V, rounded to dtype as the round
+    workloads are. Random numbers only; none of the method's arithmetic."""
+
+    def __init__(self, seed: int, chunk_tokens: int, n_heads: int, head_dim: int, dtype: str = "bf16"):
+        self.seed, self.shape, self.dtype = seed, (chunk_tokens, n_heads, head_dim), dtype
+        self._memo: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray, np.ndarray]] = {}
+
+    def __call__(self, c: int, s: int):
+        key = (c, s)
+        if key not in self._memo:
+            rng = np.random.default_rng([self.seed, c, s])
+            self._memo[key] = tuple(_normal(rng, self.shape, self.dtype) for _ in range(3))
+        return self._memo[key]
