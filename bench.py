@@ -16,9 +16,10 @@ head (padding, skipped tiles and softmax not counted). Also reported: the
 attention kernel alone against the bf16 MFMA peak (roofline, timed with
 events on the stream it runs on), chunk-rounds/s, the cache writes against
 HBM bandwidth and, unless --no-extras, the long-rollout round with 3D RoPE,
-the 14B-shaped int8-QK round and the W8A8 linears around attention (QKV and
-O projections of the round's tokens); and the fp64 oracle timed on the host
-on a bounded sample of the same round.
+the 14B-shaped int8-QK round, the W8A8 linears around attention (QKV and
+O projections of the round's tokens) and whole 1F1C rollouts (4 and 5 steps,
+133 chunks = 399 latent frames: fill, steady state, drain); and the fp64
+oracle timed on the host on a bounded sample of the same round.
 """
 from __future__ import annotations
 
@@ -379,6 +380,62 @@ def bench_w8a8(torch, wf, tokens, steps, warmup, stream):
     return out
 
 
+def bench_rollout_1f1c(torch, wf, n_steps, n_chunks, hist_window, chunk_tokens, n_heads, head_dim, stream):
+    """A whole 1F1C rollout of one layer through wf_1f1c_plan / wf_1f1c_run_round: pipeline
+    fill, steady state, drain. The null model's Q/K/V come from a device pool of seeded draws
+    reused across chunks (timing only needs the shapes); each round is timed with events."""
+    C, H, D = chunk_tokens, n_heads, head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(14)
+    P = hist_window + n_steps + 2  # distinct chunk entries, reused modulo P
+
+    def draw(rows):
+        return torch.randn(rows, H, D, generator=g, device="cuda").to(torch.bfloat16)
+
+    kpool = {(c, s): draw(C) for c in range(P) for s in range(n_steps + 1)}
+    vpool = {(c, s): draw(C) for c in range(P) for s in range(n_steps + 1)}
+    qblock = draw((n_steps + 1) * C)
+
+    def model(plan):
+        ks = [kpool[(c % P, s)] for c, s in plan.inflight]
+        vs = [vpool[(c % P, s)] for c, s in plan.inflight]
+        return qblock[:plan.n_inflight * C], ks, vs
+
+    scale = 1.0 / float(np.sqrt(D))
+    ro = wf.Rollout1F1C(n_steps, n_chunks, hist_window, C, H, D, scale, torch.bfloat16, stream=stream)
+    timers, plans = [], []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(ro.n_rounds):
+        t = Timer(torch, stream, 2)
+        t.mark(0)
+        plan, _, _ = ro.step(model)
+        t.mark(1)
+        timers.append(t)
+        plans.append((plan.n_inflight, plan.n_hist, plan.output))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = np.array([t.ms(0, 1) for t in timers])
+    flops = np.array([4.0 * D * H * sum(C * (nh + j + 1) * C for j in range(n)) for n, nh, _ in plans])
+    steady = [i for i, (n, nh, o) in enumerate(plans) if n == n_steps + 1 and nh == hist_window]
+    fill = [i for i, (_, _, o) in enumerate(plans) if o is None]
+    res = {
+        "workload": f"{n_steps}-step rollout of {n_chunks} chunks ({3 * n_chunks} latent frames), history window "
+                    f"{hist_window}, {H} heads x {D}, {C}-token chunks, one layer",
+        "rounds": ro.n_rounds, "fill_rounds": len(fill), "steady_rounds": len(steady),
+        "rollout_ms_gpu": float(ms.sum()), "rollout_s_wall": wall,
+        "round_all": ms_summary(ms),
+        "effective_tflops_whole_rollout": float(flops.sum() / (ms.sum() / 1e3) / 1e12),
+        "outputs_per_s_whole_rollout": n_chunks / (ms.sum() / 1e3),
+    }
+    if steady:
+        sm = ms[steady]
+        res["round_steady"] = ms_summary(sm)
+        res["steady_outputs_per_s"] = 1e3 / float(np.median(sm))
+        res["steady_effective_tflops"] = float(flops[steady[0]] / (np.median(sm) / 1e3) / 1e12)
+    return res
+
+
 def bench_power(torch, wf, cfg, seconds):
     """Board power while the headline attention runs back to back, and energy per launch."""
     from chunk_causal_dit_amd.profiling import sample_power
@@ -428,10 +485,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=4680, help="query rows per chunk in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the rollout, int8-QK and W8A8 measurements")
+    ap.add_argument("--no-extras", action="store_true", help="skip the rollout, int8-QK, W8A8 and 1F1C rollout measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0, help="run a plain copy of this size first")
     ap.add_argument("--w8a8-only", action="store_true",
                     help="run only the W8A8 linear measurement and print its JSON (for profiling)")
+    ap.add_argument("--rollout-only", action="store_true",
+                    help="run only the 1F1C rollout measurement and print its JSON (for profiling)")
     ap.add_argument("--power-seconds", type=float, default=3.0,
                     help="seconds of back-to-back attention launches with the board power sensor read (0: off)")
     args = ap.parse_args()
@@ -458,6 +517,11 @@ def main():
     cfg = CONFIGS["wan13b_4step"]
     if args.w8a8_only:
         print(json.dumps({"w8a8": bench_w8a8(torch, wf, cfg.nq, args.steps, args.warmup, stream)}), flush=True)
+        return
+    if args.rollout_only:
+        print(json.dumps({"rollout_1f1c": {
+            "4step": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream)}}),
+            flush=True)
         return
     inp, ms_per_step, kv_ms, attn_ms = bench_round(torch, wf, cfg, args.steps, args.warmup, stream)
     print(f"[bench] {cfg.name}: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
@@ -522,6 +586,11 @@ def main():
         print("[bench] int8-QK done", file=sys.stderr, flush=True)
         res["w8a8"] = bench_w8a8(torch, wf, cfg.nq, 20, 3, stream)
         print("[bench] W8A8 linears done", file=sys.stderr, flush=True)
+        res["rollout_1f1c"] = {
+            "4step": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream),
+            "5step": bench_rollout_1f1c(torch, wf, 5, 133, 3, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream),
+        }
+        print("[bench] 1F1C rollouts done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
     print(json.dumps(res), flush=True)
