@@ -20,7 +20,8 @@
 //     16 different bank groups while each copy instruction still reads whole
 //     64-byte row segments from HBM;
 //   * epilogue in fp32: (float)acc * (s_x[m] * s_w[n]) + bias[n], rounded to
-//     bf16, staged through LDS and stored as full 16-byte row pieces;
+//     bf16, staged through LDS (rows padded to 520 bytes: conflict-free 8-byte
+//     writes) and stored as full 16-byte row pieces;
 //   * XCD-aware tile order: each XCD gets one contiguous run of a banded
 //     order (4 tile rows at a time), so the tiles it runs together share
 //     operands in its L2.
@@ -38,38 +39,60 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- row quantization
 // One wave per row: s = amax / 127 (1 when amax = 0), code = clamp(rint(x / s), +-127),
-// fp32 decisions with a correctly rounded division. cols % 8 == 0.
+// fp32 decisions with a correctly rounded division. cols % 8 == 0. Rows of up to
+// NP * 512 columns are read from HBM once and kept in registers (16-byte pieces,
+// piece p of lane l at column 512 p + 8 l); NP is picked per launch from cols, so a
+// short row holds few registers (and more waves fit); longer rows are read twice.
+constexpr int RPIECES_MAX = 16;
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint2 quant_piece(const u32x4& raw, float s) {
+  unsigned w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (e & 1) ? bf16_hi(raw[e >> 1]) : bf16_lo(raw[e >> 1]);
+    const int code = (int)fminf(fmaxf(rintf(x / s), -127.f), 127.f);
+    w[e >> 2] |= (unsigned)(code & 0xff) << (8 * (e & 3));
+  }
+  return uint2{w[0], w[1]};
+}
+
+__device__ __forceinline__ float piece_amax(const u32x4& raw, float amax) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[e])), fabsf(bf16_hi(raw[e]))));
+  return amax;
+}
+
+template <int RPIECES>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const __bf16* __restrict__ x, int rows, int cols,
                                                          signed char* __restrict__ q, float* __restrict__ scales) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const __bf16* xr = x + (size_t)row * cols;
+  signed char* qr = q + (size_t)row * cols;
+  u32x4 held[RPIECES];
   float amax = 0.f;
-  for (int c = lane * 8; c < cols; c += 512) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(raw[e] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(raw[e] & 0xffff0000u)));
-    }
+  for (int p = 0; p < RPIECES; ++p) {
+    const int c = p * 512 + lane * 8;
+    held[p] = c < cols ? *reinterpret_cast<const u32x4*>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+    amax = piece_amax(held[p], amax);
   }
+  for (int c = RPIECES * 512 + lane * 8; c < cols; c += 512)  // rows longer than the register set
+    amax = piece_amax(*reinterpret_cast<const u32x4*>(xr + c), amax);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   const float s = amax > 0.f ? amax / 127.0f : 1.0f;
   if (lane == 0) scales[row] = s;
-  signed char* qr = q + (size_t)row * cols;
-  for (int c = lane * 8; c < cols; c += 512) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + c);
-    unsigned w[2] = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const unsigned bits = (e & 1) ? (raw[e >> 1] & 0xffff0000u) : (raw[e >> 1] << 16);
-      const float v = rintf(__uint_as_float(bits) / s);
-      const int code = (int)fminf(fmaxf(v, -127.f), 127.f);
-      w[e >> 2] |= (unsigned)(code & 0xff) << (8 * (e & 3));
-    }
-    *reinterpret_cast<uint2*>(qr + c) = uint2{w[0], w[1]};
+  for (int p = 0; p < RPIECES; ++p) {
+    const int c = p * 512 + lane * 8;
+    if (c < cols) *reinterpret_cast<uint2*>(qr + c) = quant_piece(held[p], s);
   }
+  for (int c = RPIECES * 512 + lane * 8; c < cols; c += 512)
+    *reinterpret_cast<uint2*>(qr + c) = quant_piece(*reinterpret_cast<const u32x4*>(xr + c), s);
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -79,7 +102,8 @@ constexpr int NST = 3;                      // LDS stages
 constexpr int TILE_A = BM * BK, TILE_B = BN * BK;
 constexpr int STAGE = TILE_A + TILE_B;      // 32 KB
 constexpr int LDS_MAIN = NST * STAGE;
-constexpr int OUT_LD = BN + 8;              // bf16 staging row stride (elements); 528 bytes
+constexpr int OUT_LD = BN + 4;              // bf16 staging row stride (elements): 520 bytes, so the
+                                            // 32 rows of one 8-byte write hit 32 different bank pairs
 constexpr int LDS_OUT = BM * OUT_LD * 2;
 constexpr int LDS_BYTES = LDS_OUT > LDS_MAIN ? LDS_OUT : LDS_MAIN;
 constexpr int COPIES = 2 * (BM / 16) / NWV;  // copy instructions per wave per stage (A and B)
@@ -296,8 +320,11 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
   for (int idx = tid; idx < PIECES; idx += NWV * 64) {
     const int rl = idx / (BN / 8), cp = idx % (BN / 8);
     const int m = m0 + rl, n = n0 + cp * 8;
-    if (m < M && n < N)
-      *reinterpret_cast<u32x4*>(yo + (size_t)m * N + n) = *reinterpret_cast<const u32x4*>(out_lds + rl * OUT_LD + cp * 8);
+    if (m < M && n < N) {
+      const uint2* src = reinterpret_cast<const uint2*>(out_lds + rl * OUT_LD + cp * 8);  // 8-byte aligned
+      const uint2 lo = src[0], hi = src[1];
+      *reinterpret_cast<u32x4*>(yo + (size_t)m * N + n) = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
   }
 }
 
@@ -306,9 +333,21 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 namespace wf {
 
 hipError_t launch_quant_rows_i8(const void* x, int rows, int cols, void* q, float* scales, hipStream_t s) {
-  quant_rows_kernel<<<(rows + 3) / 4, 256, 0, s>>>(static_cast<const __bf16*>(x), rows, cols,
-                                                    static_cast<signed char*>(q), scales);
-  return hipGetLastError();
+  const int pieces = (cols + 511) / 512;
+  auto run = [&](auto kern) {
+    kern<<<(rows + 3) / 4, 256, 0, s>>>(static_cast<const __bf16*>(x), rows, cols, static_cast<signed char*>(q),
+                                        scales);
+    return hipGetLastError();
+  };
+  if (pieces <= 1) return run(quant_rows_kernel<1>);
+  if (pieces <= 2) return run(quant_rows_kernel<2>);
+  if (pieces <= 3) return run(quant_rows_kernel<3>);
+  if (pieces <= 4) return run(quant_rows_kernel<4>);
+  if (pieces <= 6) return run(quant_rows_kernel<6>);
+  if (pieces <= 8) return run(quant_rows_kernel<8>);
+  if (pieces <= 10) return run(quant_rows_kernel<10>);
+  if (pieces <= 12) return run(quant_rows_kernel<12>);
+  return run(quant_rows_kernel<RPIECES_MAX>);
 }
 
 hipError_t launch_gemm_w8a8(const void* xq, const float* sx, const void* wq, const float* sw, const void* bias, int M,
