@@ -10,15 +10,17 @@
 //     32 x 32), v_mfma_i32_32x32x32_i8, one wave per SIMD: the large wave
 //     tile keeps LDS reads at 64 B/clk per CU at full MFMA rate (LDS serves
 //     about 128 B/clk, and the HBM -> LDS copies take another 32);
-//   * K advances 64 bytes per stage; three LDS stages of A and B (32 KB
-//     each) filled by direct HBM -> LDS copies (global_load_lds_dwordx4);
-//     the operands of the next k32 step are read into a second register set
-//     while the MFMAs of the current one run, and the one barrier per stage
-//     sits between the two k32 steps, where the stage's buffer is free to refill;
-//   * LDS tile rows are 64 bytes (four 16-byte pieces); piece p of row r sits
-//     in slot p ^ ((r >> 2) & 3), so the 16 lanes of an MFMA operand read hit
-//     16 different bank groups while each copy instruction still reads whole
-//     64-byte row segments from HBM;
+//   * K advances 128 bytes per stage (K % 128 == 0; gemm_w8a8_k128_kernel)
+//     through two 64 KB LDS stages of A and B, or 64 bytes per stage through
+//     three 32 KB stages otherwise (gemm_w8a8_kernel), filled by direct
+//     HBM -> LDS copies (global_load_lds_dwordx4); the operands of the next
+//     k32 step are read into a second register set while the MFMAs of the
+//     current one run, and the one barrier per stage sits before its last k32
+//     step, where the stage's buffer is free to refill;
+//   * LDS tile rows are 128 (64) bytes; piece p of row r sits in slot
+//     p ^ ((r >> 1) & 7) (p ^ ((r >> 2) & 3)), so the 16 lanes of an MFMA
+//     operand read hit 16 different bank groups while each copy instruction
+//     still reads whole row segments from HBM;
 //   * epilogue in fp32: (float)acc * (s_x[m] * s_w[n]) + bias[n], rounded to
 //     bf16, staged through LDS (rows padded to 520 bytes: conflict-free 8-byte
 //     writes) and stored as full 16-byte row pieces;
@@ -160,6 +162,75 @@ __device__ __forceinline__ void tile_of(int b, int tm_count, int tn_count, int& 
   tn = in / rows;
 }
 
+// Epilogue of a 256 x 256 tile held as acc[i][j] by 4 waves (layout as in the kernels
+// below): the raw int32 accumulators, or the fp32 scale/bias step rounded to bf16,
+// staged through LDS and stored as 16-byte row pieces. The tile's LDS stages must no
+// longer be read when it starts.
+template <bool OUT_I32>
+__device__ __forceinline__ void gemm_epilogue(const i32x16 (&acc)[4][4], char* lds, const float* __restrict__ sx,
+                                              const float* __restrict__ sw, const __bf16* __restrict__ bias, int M,
+                                              int N, int m0, int n0, int wm, int wn, int rr, int hh, int tid,
+                                              void* __restrict__ y) {
+  if constexpr (OUT_I32) {
+    int* yo = static_cast<int*>(y);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 128 + 32 * i + rr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * 128 + 32 * j + 8 * g + 4 * hh;
+          if (n < N)
+            *reinterpret_cast<i32x4*>(yo + (size_t)m * N + n) =
+                i32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+    }
+    return;
+  }
+  // fp32 epilogue into the bf16 staging tile [BM][OUT_LD] (the stages are no longer read)
+  __bf16* out_lds = reinterpret_cast<__bf16*>(lds);
+  float sxm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sxm[i] = sx[min(m0 + wm * 128 + 32 * i + rr, M - 1)];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn * 128 + 32 * j + 8 * g + 4 * hh;
+      float swn[4], bn[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = min(n0 + nl + c, N - 1);
+        swn[c] = sw[n];
+        bn[c] = bias ? (float)bias[n] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ml = wm * 128 + 32 * i + rr;
+        __bf16 v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = (__bf16)fmaf((float)acc[i][j][4 * g + c], sxm[i] * swn[c], bn[c]);
+        *reinterpret_cast<uint2*>(out_lds + ml * OUT_LD + nl) = *reinterpret_cast<const uint2*>(v);
+      }
+    }
+  __syncthreads();
+  // coalesced stores: 16-byte pieces (8 columns) of each row
+  __bf16* yo = static_cast<__bf16*>(y);
+  constexpr int PIECES = BM * BN / 8;
+#pragma unroll 4
+  for (int idx = tid; idx < PIECES; idx += NWV * 64) {
+    const int rl = idx / (BN / 8), cp = idx % (BN / 8);
+    const int m = m0 + rl, n = n0 + cp * 8;
+    if (m < M && n < N) {
+      const uint2* src = reinterpret_cast<const uint2*>(out_lds + rl * OUT_LD + cp * 8);  // 8-byte aligned
+      const uint2 lo = src[0], hi = src[1];
+      *reinterpret_cast<u32x4*>(yo + (size_t)m * N + n) = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  }
+}
+
 template <bool OUT_I32>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w8a8_kernel(
     const signed char* __restrict__ xq, const float* __restrict__ sx, const signed char* __restrict__ wq,
@@ -268,64 +339,141 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
   for (; kt < KT; ++kt, s = s == NST - 1 ? 0 : s + 1) body(std::false_type{}, kt, s);
   __syncthreads();
 
-  if constexpr (OUT_I32) {
-    int* yo = static_cast<int*>(y);
+  gemm_epilogue<OUT_I32>(acc, lds, sx, sw, bias, M, N, m0, n0, wm, wn, rr, hh, tid, y);
+}
+
+// ---------------------------------------------------------------- GEMM, 128-byte K stages
+// Same tile, waves and epilogue as above, with K advancing 128 bytes per stage through
+// two 64 KB LDS stages: one barrier per 64 MFMAs of a wave instead of per 32. LDS rows
+// are 128 bytes (eight 16-byte pieces); piece p of row r sits in slot p ^ ((r >> 1) & 7),
+// which keeps the 16 lanes of each operand read on 16 different bank groups.
+constexpr int BK2 = 128;
+constexpr int TILE_A2 = BM * BK2, TILE_B2 = BN * BK2;
+constexpr int STAGE2 = TILE_A2 + TILE_B2;  // 64 KB
+constexpr int LDS2_MAIN = 2 * STAGE2;
+constexpr int LDS2_BYTES = LDS_OUT > LDS2_MAIN ? LDS_OUT : LDS2_MAIN;
+static_assert(LDS2_BYTES <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ int slot2_of(int r, int p) { return p ^ ((r >> 1) & 7); }
+
+// Copy instruction j (0..31) of one operand covers rows 8j .. 8j+7 of the 128-byte K
+// slice [k0, k0+128); lane i takes slot i % 8 of row 8j + i / 8, i.e. the piece
+// slot2_of(row, i % 8). Wave w issues instructions w + 4u, u = 0..7.
+__device__ __forceinline__ void copy2_piece(const signed char* src, int rows, int row0, int K, int k0, char* lds,
+                                            int wave, int lane, int u) {
+  const int j = wave + u * NWV;
+  const int r = 8 * j + (lane >> 3);
+  const int p = slot2_of(r, lane & 7);
+  const int gr = min(row0 + r, rows - 1);
+  __builtin_amdgcn_global_load_lds(src + (size_t)gr * K + k0 + p * 16, (LDS_AS void*)(lds + j * 1024), 16, 0, 0);
+}
+
+template <bool OUT_I32>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w8a8_k128_kernel(
+    const signed char* __restrict__ xq, const float* __restrict__ sx, const signed char* __restrict__ wq,
+    const float* __restrict__ sw, const __bf16* __restrict__ bias, int M, int N, int K, void* __restrict__ y) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int rr = lane & 31, hh = lane >> 5;
+  char* lds = g_lds;
+  const int KT = K / BK2;
+
+  auto copy_stage = [&](int kt, char* st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + 32 * i + rr;
-      if (m >= M) continue;
+    for (int u = 0; u < 8; ++u) copy2_piece(xq, M, m0, K, kt * BK2, st, wave, lane, u);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int u = 0; u < 8; ++u) copy2_piece(wq, N, n0, K, kt * BK2, st + TILE_A2, wave, lane, u);
+  };
+  // operand rows: A row wm*128 + 32i + rr, B row wn*128 + 32j + rr; k32 step ks takes piece
+  // 2ks + hh; block i (j) adds 32 rows = 4096 bytes
+  const int x = (rr >> 1) & 7;
+  int aoff[4], boff[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 128 + 32 * j + 8 * g + 4 * hh;
-          if (n < N)
-            *reinterpret_cast<i32x4*>(yo + (size_t)m * N + n) =
-                i32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        }
-    }
-    return;
+  for (int ks = 0; ks < 4; ++ks) {
+    aoff[ks] = (wm * 128 + rr) * BK2 + 16 * ((2 * ks + hh) ^ x);
+    boff[ks] = TILE_A2 + (wn * 128 + rr) * BK2 + 16 * ((2 * ks + hh) ^ x);
   }
-  // fp32 epilogue into the bf16 staging tile [BM][OUT_LD] (the stages are no longer read)
-  __bf16* out_lds = reinterpret_cast<__bf16*>(lds);
-  float sxm[4];
+  i32x4 a0[4], b0[4], a1[4], b1[4];
+  // one read of operand q (0..7, in the order the MFMAs use them: a[0], b[0..3], a[1..3])
+  auto read_op = [&](const char* st, int ks, int q, i32x4(&av)[4], i32x4(&bv)[4]) {
+    if (q == 0) av[0] = *reinterpret_cast<const i32x4*>(st + aoff[ks]);
+    else if (q < 5) bv[q - 1] = *reinterpret_cast<const i32x4*>(st + boff[ks] + 4096 * (q - 1));
+    else av[q - 4] = *reinterpret_cast<const i32x4*>(st + aoff[ks] + 4096 * (q - 4));
+  };
+  i32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sxm[i] = sx[min(m0 + wm * 128 + 32 * i + rr, M - 1)];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int nl = wn * 128 + 32 * j + 8 * g + 4 * hh;
-      float swn[4], bn[4];
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+  auto mfma_t = [&](int t, const i32x4(&av)[4], const i32x4(&bv)[4]) {
+    acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv[t & 3], av[t >> 2], acc[t >> 2][t & 3], 0, 0, 0);
+  };
+  // a k32 step: 16 MFMAs on (av, bv), the first 8 each followed by one read of the next
+  // step's operands into (nav, nbv)
+  auto step = [&](const i32x4(&av)[4], const i32x4(&bv)[4], const char* nst, int nks, i32x4(&nav)[4],
+                  i32x4(&nbv)[4]) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int n = min(n0 + nl + c, N - 1);
-        swn[c] = sw[n];
-        bn[c] = bias ? (float)bias[n] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ml = wm * 128 + 32 * i + rr;
-        __bf16 v[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = (__bf16)fmaf((float)acc[i][j][4 * g + c], sxm[i] * swn[c], bn[c]);
-        *reinterpret_cast<uint2*>(out_lds + ml * OUT_LD + nl) = *reinterpret_cast<const uint2*>(v);
-      }
+    for (int t = 0; t < 16; ++t) {
+      mfma_t(t, av, bv);
+      if (t < 8) read_op(nst, nks, t, nav, nbv);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  copy_stage(0, lds);
+  if (KT > 1) copy_stage(1, lds + STAGE2);
+  if (KT > 1) wait_vm_barrier<16>();
+  else wait_vm_barrier<0>();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) read_op(lds, 0, q, a0, b0);
+
+  // Stage kt in buffer s: steps 0-2 each read the next step's operands; the barrier
+  // (stage kt+1 has landed, every wave's reads of stage kt are done) comes before step 3,
+  // whose MFMAs carry the reads of stage kt+1's first step and the copies that refill
+  // buffer s with stage kt+2.
+  auto body = [&](auto full, int kt, int s) {
+    const char* st = lds + s * STAGE2;
+    const char* nst = lds + (1 - s) * STAGE2;
+    step(a0, b0, st, 1, a1, b1);
+    step(a1, b1, st, 2, a0, b0);
+    step(a0, b0, st, 3, a1, b1);
+    wait_vm_barrier<0>();
+    // the asm above already drained lgkmcnt; saying so keeps the compiler from placing its
+    // own lgkmcnt(0) after the first new read of step 3
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if constexpr (decltype(full)::value) {
+      char* cst = lds + s * STAGE2;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        mfma_t(t, a1, b1);
+        if (t < 8) read_op(nst, 0, t, a0, b0);
+        if (t < 8) copy2_piece(xq, M, m0, K, (kt + 2) * BK2, cst, wave, lane, t);
+        else copy2_piece(wq, N, n0, K, (kt + 2) * BK2, cst + TILE_A2, wave, lane, t - 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      if (kt + 1 < KT) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) read_op(nst, 0, q, a0, b0);
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) mfma_t(t, a1, b1);
+    }
+  };
+  int kt = 0, s = 0;
+  for (; kt + 2 < KT; ++kt, s ^= 1) body(std::true_type{}, kt, s);
+  for (; kt < KT; ++kt, s ^= 1) body(std::false_type{}, kt, s);
   __syncthreads();
-  // coalesced stores: 16-byte pieces (8 columns) of each row
-  __bf16* yo = static_cast<__bf16*>(y);
-  constexpr int PIECES = BM * BN / 8;
-#pragma unroll 4
-  for (int idx = tid; idx < PIECES; idx += NWV * 64) {
-    const int rl = idx / (BN / 8), cp = idx % (BN / 8);
-    const int m = m0 + rl, n = n0 + cp * 8;
-    if (m < M && n < N) {
-      const uint2* src = reinterpret_cast<const uint2*>(out_lds + rl * OUT_LD + cp * 8);  // 8-byte aligned
-      const uint2 lo = src[0], hi = src[1];
-      *reinterpret_cast<u32x4*>(yo + (size_t)m * N + n) = u32x4{lo.x, lo.y, hi.x, hi.y};
-    }
-  }
+  gemm_epilogue<OUT_I32>(acc, lds, sx, sw, bias, M, N, m0, n0, wm, wn, rr, hh, tid, y);
 }
 
 }  // namespace
@@ -362,6 +510,18 @@ hipError_t launch_gemm_w8a8(const void* xq, const float* sx, const void* wq, con
                                               static_cast<const __bf16*>(bias), M, N, K, y);
     return hipGetLastError();
   };
+  if (K % BK2 == 0) {  // 128-byte stages: half the barriers per MFMA
+    auto run2 = [&](auto kern) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, LDS2_BYTES);
+      if (e != hipSuccess) return e;
+      kern<<<blocks, NWV * 64, LDS2_BYTES, s>>>(static_cast<const signed char*>(xq), sx,
+                                                 static_cast<const signed char*>(wq), sw,
+                                                 static_cast<const __bf16*>(bias), M, N, K, y);
+      return hipGetLastError();
+    };
+    return out_i32 ? run2(gemm_w8a8_k128_kernel<true>) : run2(gemm_w8a8_k128_kernel<false>);
+  }
   return out_i32 ? run(gemm_w8a8_kernel<true>) : run(gemm_w8a8_kernel<false>);
 }
 
