@@ -25,7 +25,8 @@ def _quantized(wf, x, w):
     return xq, sx, wq, sw
 
 
-@pytest.mark.parametrize("M,K", [(1, 64), (300, 1536), (257, 5120), (33, 8960)])
+# K picks the register pieces per lane of the quantizer: 1, 2, 3, 4, 8, 10, and past 16 the second read
+@pytest.mark.parametrize("M,K", [(1, 64), (70, 1024), (300, 1536), (65, 2048), (40, 4096), (257, 5120), (33, 8960)])
 def test_quant_rows_bit_exact(M, K):
     wf = RL.require_gpu()
     x, _, _ = make_linear_inputs(M, 8, K, seed=M + K)
@@ -40,7 +41,9 @@ def test_quant_rows_bit_exact(M, K):
     assert np.array_equal(scales.cpu().numpy(), rs)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 8, 64), (300, 264, 128), (513, 520, 1536), (77, 1536, 5120), (256, 256, 64)])
+# K = 64 and 192 take the 64-byte-stage kernel; 128 .. 5120 the 128-byte-stage kernel with 1, 2, 3, 12, 40 stages
+@pytest.mark.parametrize("M,N,K", [(1, 8, 64), (300, 264, 128), (260, 8, 256), (100, 520, 384), (70, 264, 192),
+                                   (513, 520, 1536), (77, 1536, 5120), (256, 256, 64)])
 def test_int32_accumulators_bit_exact(M, N, K):
     wf = RL.require_gpu()
     print(f"[case] gemm int32 M={M} N={N} K={K}", flush=True)
