@@ -382,7 +382,8 @@ def run_round(cache: KVCache, plan: RoundPlan, q: torch.Tensor, ks: Sequence[tor
               lse: Optional[torch.Tensor] = None, with_lse: bool = True, stream=None):
     """One round on the stream: append the new chunk, refresh the other in-flight entries,
     attention over the round's query block, evict. ks[i], vs[i] are this round's K/V of
-    in-flight chunk i (cleanest first). Returns (out, lse or None)."""
+    in-flight chunk i (cleanest first). With a RoPE geometry on the cache (set_rope), q is
+    rotated in place and K inside the cache writes. Returns (out, lse or None)."""
     N = plan.n_inflight
     if len(ks) != N or len(vs) != N:
         raise ValueError(f"need {N} K and V chunks, got {len(ks)} and {len(vs)}")
@@ -400,16 +401,21 @@ class Rollout1F1C:
 
     model(plan) returns the round's query block [n_inflight*C][H][D] and the lists of
     this round's K and V chunks of the in-flight chunks, cleanest first. Each call of
-    step() plans the next round (wf_1f1c_plan) and enqueues it (wf_1f1c_run_round)."""
+    step() plans the next round (wf_1f1c_plan) and enqueues it (wf_1f1c_run_round).
+    With rope (the 3D geometry of wf_kv_set_rope), the query block is rotated in place
+    each round and K inside the cache writes, at the chunks' global indices."""
 
     def __init__(self, n_steps: int, n_chunks: int, hist_window: int, chunk_tokens: int, n_heads: int,
                  head_dim: int, scale: float, dtype: torch.dtype = torch.bfloat16, n_slots: Optional[int] = None,
-                 stream=None):
+                 stream=None, rope: Optional[dict] = None):
         self.n_steps, self.n_chunks, self.hist_window, self.scale = n_steps, n_chunks, hist_window, scale
         self.n_rounds = rounds_1f1c(n_steps, n_chunks)
         plan_1f1c(n_steps, n_chunks, hist_window, 0)  # validates the window
         need = hist_window + n_steps + 1
         self.cache = KVCache(n_slots or need, chunk_tokens, n_heads, head_dim, dtype, stream=stream)
+        if rope is not None:  # {"frames_per_chunk", "grid_h", "grid_w", optional "split", "theta"}
+            self.cache.set_rope(rope["frames_per_chunk"], rope["grid_h"], rope["grid_w"],
+                                tuple(rope.get("split", (44, 42, 42))), rope.get("theta", 10000.0))
         self.round = 0
         self.stream = stream
 

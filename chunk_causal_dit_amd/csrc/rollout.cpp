@@ -63,7 +63,7 @@ WF_EXPORT int wf_1f1c_plan(int n_steps, int n_chunks, int hist_window, int round
   return WF_OK;
 }
 
-WF_EXPORT int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, const void* q, const void* const* k,
+WF_EXPORT int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void* q, const void* const* k,
                                 const void* const* v, float scale, void* out, float* lse, void* stream) {
   const char* who = "wf_1f1c_run_round";
   if (!kv || !plan || !q || !k || !v || !out) return fail(WF_E_NULL, "%s: NULL argument", who);
@@ -88,12 +88,35 @@ WF_EXPORT int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, cons
   if (append && kv->free_slots.empty()) return fail(WF_E_FULL, "%s: no free slot for the new chunk", who);
   if ((long long)N * kv->chunk_tokens * kv->n_heads * kv->head_dim >= (1LL << 40))
     return fail(WF_E_SHAPE, "%s: query block too large", who);
+  const bool rope = kv->rope.on;
+  const int first = plan->inflight_chunk[0];
+  if (rope) {
+    // the query block is rotated as one run of whole chunks: its chunk ids must be consecutive
+    for (int i = 0; i < N; ++i)
+      if (plan->inflight_chunk[i] != first + i)
+        return fail(WF_E_SHAPE, "%s: with RoPE the in-flight chunk ids must be consecutive", who);
+    if (first < 0 || (double)kv->rope.fpc * ((double)first + N + 1) > 16777216.0)
+      return fail(WF_E_SHAPE, "%s: frame positions of chunks %d .. %d exceed the exact fp32 integer range", who,
+                  first, first + N - 1);
+  }
 
   // every check passed: the calls below can fail only at launch (WF_E_HIP)
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   int st = WF_OK;
-  if (append && (st = wf_kv_append(kv, k[N - 1], v[N - 1], stream, nullptr)) != WF_OK) return st;
-  for (int i = 0; i < N - (append ? 1 : 0); ++i)
-    if ((st = wf_kv_refresh(kv, Hs + i, k[i], v[i], stream)) != WF_OK) return st;
+  if (rope) {
+    const wf::RopeConfig& rc = kv->rope;
+    hipError_t e = wf::launch_rope3d(q, N * kv->chunk_tokens, kv->n_heads, kv->head_dim, kv->dtype, first, rc.fpc,
+                                     rc.gh, rc.gw, rc.table, hs);
+    if (e != hipSuccess) return fail(WF_E_HIP, "%s: rope launch failed: %s", who, hipGetErrorString(e));
+    if (append && (st = wf_kv_append_rope(kv, k[N - 1], v[N - 1], first + N - 1, stream, nullptr)) != WF_OK)
+      return st;
+    for (int i = 0; i < N - (append ? 1 : 0); ++i)
+      if ((st = wf_kv_refresh_rope(kv, Hs + i, k[i], v[i], first + i, stream)) != WF_OK) return st;
+  } else {
+    if (append && (st = wf_kv_append(kv, k[N - 1], v[N - 1], stream, nullptr)) != WF_OK) return st;
+    for (int i = 0; i < N - (append ? 1 : 0); ++i)
+      if ((st = wf_kv_refresh(kv, Hs + i, k[i], v[i], stream)) != WF_OK) return st;
+  }
   if ((st = wf_chunk_causal_attn_fwd(q, kv, N, scale, out, lse, stream)) != WF_OK) return st;
   return wf_kv_evict(kv, plan->evict_after);
 }

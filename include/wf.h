@@ -294,10 +294,14 @@ int wf_1f1c_plan(int n_steps, int n_chunks, int hist_window, int round, wf_round
  * evict plan->evict_after oldest entries. The cache table must hold the
  * previous round's state: n_hist + n_inflight entries, less one when a chunk
  * is appended. k and v are host arrays of n_inflight device pointers.
+ * With a RoPE geometry on the cache (wf_kv_set_rope), the query block is
+ * first rotated in place (chunk ids inflight_chunk[0] .. as global chunk
+ * indices, which must be consecutive) and K is rotated inside the cache
+ * writes (wf_kv_append_rope / wf_kv_refresh_rope); V is written as is.
  * Every argument is checked before anything is enqueued (WF_E_NULL,
  * WF_E_SHAPE, WF_E_FULL; the cache is unchanged on these); WF_E_HIP means a
  * launch was rejected after earlier steps of the round were enqueued. */
-int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, const void* q, const void* const* k,
+int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void* q, const void* const* k,
                       const void* const* v, float scale, void* out, float* lse, void* stream);
 
 /* ---- diagnostics ---- */

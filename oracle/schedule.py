@@ -35,6 +35,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 from .attention import chunk_causal_attention
+from .rope import rope3d
 
 __all__ = ["timesteps", "n_rounds", "round_plan", "rollout_attention"]
 
@@ -81,25 +82,34 @@ def rollout_attention(n_steps: int, n_chunks: int, hist_window: int,
                       qkv: Callable[[int, int], Tuple[np.ndarray, np.ndarray, np.ndarray]],
                       scale: float, rounds: Optional[Sequence[int]] = None,
                       rows: Optional[Callable[[int], Optional[np.ndarray]]] = None,
-                      workers: int = 1) -> Dict[int, Tuple[np.ndarray, np.ndarray, Dict]]:
+                      workers: int = 1, rope: Optional[Dict] = None) -> Dict[int, Tuple[np.ndarray, np.ndarray, Dict]]:
     """Attention of every round of the rollout with a given per-(chunk, stage) model.
 
     qkv(c, s) returns the chunk's Q, K, V [C][H][D] at stage s (s = S: clean, the
-    refresh pass). History entries hold the clean K/V, qkv(c, S). Returns
-    {round: (O, LSE, plan)} for the asked rounds (default all).
+    refresh pass). History entries hold the clean K/V, qkv(c, S). With rope
+    (frames_per_chunk, grid_h, grid_w, optional split and theta), Q and K of chunk c
+    are rotated at the positions of global chunk c (oracle.rope, the 3D convention
+    of the round workloads), whatever the stage. Returns {round: (O, LSE, plan)} for
+    the asked rounds (default all).
     """
+    def rotate(x, c):
+        if rope is None:
+            return x
+        return rope3d(x, c, x.shape[0], rope["frames_per_chunk"], rope["grid_h"], rope["grid_w"],
+                      tuple(rope.get("split", (44, 42, 42))), rope.get("theta", 10000.0))
+
     out = {}
     for r in (range(n_rounds(n_steps, n_chunks)) if rounds is None else rounds):
         plan = round_plan(n_steps, n_chunks, hist_window, r)
         q_parts, k_parts, v_parts = [], [], []
         for c in plan["hist"]:
             _, k, v = qkv(c, n_steps)
-            k_parts.append(k)
+            k_parts.append(rotate(k, c))
             v_parts.append(v)
         for c, s in plan["inflight"]:
             q, k, v = qkv(c, s)
-            q_parts.append(q)
-            k_parts.append(k)
+            q_parts.append(rotate(q, c))
+            k_parts.append(rotate(k, c))
             v_parts.append(v)
         C = q_parts[0].shape[0]
         o, lse = chunk_causal_attention(np.concatenate(q_parts), np.concatenate(k_parts),

@@ -29,12 +29,12 @@ class DeviceModel:
         return torch.cat([p[0] for p in parts]), [p[1] for p in parts], [p[2] for p in parts]
 
 
-def run_rollout(wf, S, F, W, C, H, D, dtype, seed, rows=None, check_rounds=None):
+def run_rollout(wf, S, F, W, C, H, D, dtype, seed, rows=None, check_rounds=None, rope=None):
     host = NullModel(seed, C, H, D, dtype)
     tdt = RL.torch_dtype(dtype)
     model = DeviceModel(host, S, tdt)
     scale = 1.0 / np.sqrt(D)
-    ro = wf.Rollout1F1C(S, F, W, C, H, D, scale, tdt)
+    ro = wf.Rollout1F1C(S, F, W, C, H, D, scale, tdt, rope=rope)
     got, outputs = {}, []
     for _ in range(ro.n_rounds):
         plan, out, lse = ro.step(model, with_lse=True)
@@ -46,7 +46,8 @@ def run_rollout(wf, S, F, W, C, H, D, dtype, seed, rows=None, check_rounds=None)
             l = lse if sel is None else lse[:, sel]
             got[plan.round] = (o.float().cpu().numpy(), l.cpu().numpy(), plan.inflight, plan.hist)
     torch.cuda.synchronize()
-    ref = SC.rollout_attention(S, F, W, host, scale, rounds=sorted(got), rows=rows, workers=RL.oracle_workers())
+    ref = SC.rollout_attention(S, F, W, host, scale, rounds=sorted(got), rows=rows, workers=RL.oracle_workers(),
+                               rope=rope)
     for r, (o, l, inflight, hist) in got.items():
         ro_, rl_, plan = ref[r]
         assert inflight == plan["inflight"] and hist == plan["hist"]
@@ -83,3 +84,14 @@ def test_wan13b_4step_rollout_sampled():
         return RL.boundary_rows(C, n, 4, seed=r)
 
     run_rollout(wf, 4, 6, 2, C, 12, 128, "bf16", seed=91, rows=rows, check_rounds={0, 3, 4, 5, 8})
+
+
+@pytest.mark.parametrize("S,F,W,dtype,D", [(4, 6, 2, "bf16", 128), (5, 7, 3, "f32", 64)])
+def test_rollout_with_rope_every_round(S, F, W, dtype, D):
+    """3D RoPE through the runner: the query block rotated in place, K inside the cache
+    writes, at the chunks' global indices (3 frames of 4 x 8 latent tokens per chunk)."""
+    wf = RL.require_gpu()
+    print(f"[case] rope rollout S={S} F={F} W={W} {dtype} D={D}", flush=True)
+    split = (44, 42, 42) if D == 128 else (22, 22, 20)
+    rope = {"frames_per_chunk": 3, "grid_h": 4, "grid_w": 8, "split": split, "theta": 10000.0}
+    run_rollout(wf, S, F, W, 96, 2, D, dtype, seed=80 + S, rope=rope)

@@ -114,6 +114,52 @@ def test_rollout_attention_matches_scalar_assembly():
                     assert abs(lse[h, qi * C + t] - (m + math.log(z))) < 1e-12
 
 
+def test_rollout_attention_with_rope_matches_scalar_rotation():
+    """With rope, chunk c's Q and K are rotated at global chunk c: here each pair is rotated
+    by explicit cos/sin of the pages-independent angle list (rotation_angles), then the
+    round's attention is built from the definition as above."""
+    from oracle.rope import rotation_angles
+    S, F, W, fpc, gh, gw, H, D = 2, 4, 1, 1, 2, 2, 1, 8
+    C = fpc * gh * gw
+    split = (4, 2, 2)
+    qkv = _qkv_model(S, C, H, D)
+    scale = 0.5
+    rope = {"frames_per_chunk": fpc, "grid_h": gh, "grid_w": gw, "split": split, "theta": 100.0}
+    res = SC.rollout_attention(S, F, W, qkv, scale, rope=rope)
+
+    def rot(x, c):
+        y = np.array(x, dtype=np.float64)
+        for t in range(C):
+            pos = (fpc * c + t // (gh * gw), (t // gw) % gh, t % gw)
+            ang = rotation_angles(pos, split, 100.0)
+            for h in range(H):
+                for i, a in enumerate(ang):
+                    x0, x1 = x[t, h, 2 * i], x[t, h, 2 * i + 1]
+                    y[t, h, 2 * i] = x0 * math.cos(a) - x1 * math.sin(a)
+                    y[t, h, 2 * i + 1] = x0 * math.sin(a) + x1 * math.cos(a)
+        return y
+
+    for r, (o, lse, plan) in res.items():
+        for qi, (c, s) in enumerate(plan["inflight"]):
+            keys, vals = [], []
+            for hc in plan["hist"]:
+                _, k, v = qkv(hc, S)
+                keys += list(rot(k, hc))
+                vals += list(v)
+            for c2, s2 in plan["inflight"]:
+                if c2 <= c:
+                    _, k, v = qkv(c2, s2)
+                    keys += list(rot(k, c2))
+                    vals += list(v)
+            q = rot(qkv(c, s)[0], c)
+            for t in range(C):
+                logits = [scale * float(np.dot(q[t, 0], kk[0])) for kk in keys]
+                m = max(logits)
+                w = [math.exp(x - m) for x in logits]
+                ref = sum(wi * vv[0] for wi, vv in zip(w, vals)) / sum(w)
+                assert np.allclose(o[qi * C + t, 0], ref, atol=1e-12)
+
+
 @pytest.mark.parametrize("kind", ["noisiest_first", "refresh_late", "window_plus_one", "refresh_chunk_in_history",
                                   "window_slice_wraps"])
 def test_planted_mistakes_are_caught(kind):

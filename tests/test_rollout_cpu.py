@@ -95,3 +95,23 @@ def test_run_round_full_cache(L):
     assert L.wf_1f1c_run_round(h, ctypes.byref(plan), a, ptrs, ptrs, 0.1, a, None, None) == WF_E_FULL
     assert table(L, h) == [0]
     L.wf_kv_cache_destroy(h)
+
+
+def test_run_round_rope_checks(L):
+    """With a RoPE geometry the in-flight chunk ids must be consecutive and their frame
+    positions exact in fp32; both are refused before anything is enqueued."""
+    h, pools = make_cache(L, n_slots=8, C=64, H=2, D=64)
+    assert L.wf_kv_set_rope(h, 1, 8, 8, 22, 22, 20, 1e4) == WF_OK
+    a = ctypes.c_void_p(pools.k.value)
+    one = (ctypes.c_void_p * 1)(a.value)
+    plan = wf.plan_1f1c(4, 6, 2, 0)
+    plan.inflight_chunk[0] = 1 << 24  # frame position 2^24 and beyond: not exact in fp32
+    assert L.wf_1f1c_run_round(h, ctypes.byref(plan), a, one, one, 0.1, a, None, None) == WF_E_SHAPE
+    arr = (ctypes.c_int * 1)(0)
+    assert L.wf_kv_set_table(h, arr, 1) == WF_OK
+    plan1 = wf.plan_1f1c(4, 6, 2, 1)  # chunks 0, 1 in flight
+    plan1.inflight_chunk[1] = 5  # not consecutive
+    two = (ctypes.c_void_p * 2)(a.value, a.value)
+    assert L.wf_1f1c_run_round(h, ctypes.byref(plan1), a, two, two, 0.1, a, None, None) == WF_E_SHAPE
+    assert table(L, h) == [0]
+    L.wf_kv_cache_destroy(h)
