@@ -380,7 +380,8 @@ def bench_w8a8(torch, wf, tokens, steps, warmup, stream):
     return out
 
 
-def bench_rollout_1f1c(torch, wf, n_steps, n_chunks, hist_window, chunk_tokens, n_heads, head_dim, stream):
+def bench_rollout_1f1c(torch, wf, n_steps, n_chunks, hist_window, chunk_tokens, n_heads, head_dim, stream,
+                       rope=None):
     """A whole 1F1C rollout of one layer through wf_1f1c_plan / wf_1f1c_run_round: pipeline
     fill, steady state, drain. The null model's Q/K/V come from a device pool of seeded draws
     reused across chunks (timing only needs the shapes); each round is timed with events."""
@@ -402,7 +403,7 @@ def bench_rollout_1f1c(torch, wf, n_steps, n_chunks, hist_window, chunk_tokens, 
         return qblock[:plan.n_inflight * C], ks, vs
 
     scale = 1.0 / float(np.sqrt(D))
-    ro = wf.Rollout1F1C(n_steps, n_chunks, hist_window, C, H, D, scale, torch.bfloat16, stream=stream)
+    ro = wf.Rollout1F1C(n_steps, n_chunks, hist_window, C, H, D, scale, torch.bfloat16, stream=stream, rope=rope)
     timers, plans = [], []
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -421,7 +422,8 @@ def bench_rollout_1f1c(torch, wf, n_steps, n_chunks, hist_window, chunk_tokens, 
     fill = [i for i, (_, _, o) in enumerate(plans) if o is None]
     res = {
         "workload": f"{n_steps}-step rollout of {n_chunks} chunks ({3 * n_chunks} latent frames), history window "
-                    f"{hist_window}, {H} heads x {D}, {C}-token chunks, one layer",
+                    f"{hist_window}, {H} heads x {D}, {C}-token chunks, one layer"
+                    + (", 3D RoPE (query block rotated in place, K in the cache writes)" if rope else ""),
         "rounds": ro.n_rounds, "fill_rounds": len(fill), "steady_rounds": len(steady),
         "rollout_ms_gpu": float(ms.sum()), "rollout_s_wall": wall,
         "round_all": ms_summary(ms),
@@ -589,6 +591,8 @@ def main():
         res["rollout_1f1c"] = {
             "4step": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream),
             "5step": bench_rollout_1f1c(torch, wf, 5, 133, 3, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream),
+            "4step_rope": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream,
+                                             rope={"frames_per_chunk": 3, "grid_h": 30, "grid_w": 52}),
         }
         print("[bench] 1F1C rollouts done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
