@@ -48,6 +48,7 @@ METRIC = "effective attention TFLOP/s per 1F1C round (% bf16 MFMA peak); chunk-r
 PROFILES = os.path.join(ROOT, "profiles")
 ATTN_SRC = os.path.join(ROOT, "chunk_causal_dit_amd", "csrc", "attn_fwd.hip")
 ATTN_KERNEL = "attn_fwd_bf16_kernel<128, 8, true, false>"
+MERGE_KERNEL = "attn_combine_kernel<128>"
 
 
 def effective_pairs_per_head(cfg: RoundConfig) -> int:
@@ -155,8 +156,9 @@ def dev_bf16(torch, a):
     return torch.from_numpy(a).to("cuda").to(torch.bfloat16)
 
 
-def bench_round(torch, wf, cfg, steps, warmup, stream):
-    """The headline step; returns timings and the resident state."""
+def bench_round(torch, wf, cfg, steps, warmup, stream, split=True):
+    """The headline step; returns timings and the resident state. split: attention through
+    the workspace call (key split of in-flight chunk 0)."""
     C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
     inp = make_round_inputs(cfg)
     q, k_in, v_in = (dev_bf16(torch, a) for a in (inp.q, inp.k_in, inp.v_in))
@@ -171,6 +173,7 @@ def bench_round(torch, wf, cfg, steps, warmup, stream):
         cache.append(kc[j], vc[j])
     out = torch.empty_like(q)
     lse = torch.empty((H, N * C), dtype=torch.float32, device="cuda")
+    ws = wf.attn_fwd_workspace(cache) if split else None
 
     def step(t=None):
         if t:
@@ -180,7 +183,7 @@ def bench_round(torch, wf, cfg, steps, warmup, stream):
             cache.refresh(Hs + j, kc[j], vc[j])
         if t:
             t.mark(1)
-        wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, lse=lse)
+        wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, lse=lse, workspace=ws)
         if t:
             t.mark(2)
         cache.evict(1)                                  # the refresh chunk is history from now on
@@ -199,14 +202,14 @@ def bench_round(torch, wf, cfg, steps, warmup, stream):
     return inp, wall * 1e3 / steps, kv_ms, attn_ms
 
 
-def bench_rollout(torch, wf, cfg, rounds, warmup, stream, fused=False):
+def bench_rollout(torch, wf, cfg, rounds, warmup, stream, fused=False, split=True):
     """Long-rollout steady state on a permuted 12-slot ring: per round rope3d(Q), rope3d(K),
     append, refresh, attention, evict; with fused=True, K is rotated inside the cache writes
     (append_rope / refresh_rope) instead. Timing only (the values are those of round 0,
     rotated again every round)."""
     from workloads import slot_permutation
     C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
-    fpc, gh, gw, split = cfg.frames_per_chunk, cfg.grid_h, cfg.grid_w, cfg.rope_split
+    fpc, gh, gw, rsplit = cfg.frames_per_chunk, cfg.grid_h, cfg.grid_w, cfg.rope_split
     k0, v0 = make_rollout_init(cfg)
     kd, vd = dev_bf16(torch, k0), dev_bf16(torch, v0)
     del k0, v0
@@ -214,20 +217,21 @@ def bench_rollout(torch, wf, cfg, rounds, warmup, stream, fused=False):
     cache = wf.KVCache(cfg.slots, C, H, D, torch.bfloat16)
     cache.set_table(slot_permutation(cfg.slots, seed=cfg.seed)[:n0])
     if fused:
-        cache.set_rope(fpc, gh, gw, split)
+        cache.set_rope(fpc, gh, gw, rsplit)
     for g in range(n0):
         cache.refresh(g, kd[g * C:(g + 1) * C], vd[g * C:(g + 1) * C])
     q, k, v = (dev_bf16(torch, a) for a in make_rollout_round(cfg, 0))
     out = torch.empty_like(q)
     lse = torch.empty((H, N * C), dtype=torch.float32, device="cuda")
+    ws = wf.attn_fwd_workspace(cache) if split else None
 
     def one(r, t=None):
         first = r + Hs
         if t:
             t.mark(0)
-        wf.rope3d(q, first, fpc, gh, gw, split)
+        wf.rope3d(q, first, fpc, gh, gw, rsplit)
         if not fused:
-            wf.rope3d(k, first, fpc, gh, gw, split)
+            wf.rope3d(k, first, fpc, gh, gw, rsplit)
         if t:
             t.mark(1)
         if fused:
@@ -240,7 +244,7 @@ def bench_rollout(torch, wf, cfg, rounds, warmup, stream, fused=False):
                 cache.refresh(Hs + j, k[j * C:(j + 1) * C], v[j * C:(j + 1) * C])
         if t:
             t.mark(2)
-        wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, lse=lse)
+        wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, lse=lse, workspace=ws)
         if t:
             t.mark(3)
         cache.evict(1)
@@ -381,7 +385,7 @@ def bench_w8a8(torch, wf, tokens, steps, warmup, stream):
 
 
 def bench_rollout_1f1c(torch, wf, n_steps, n_chunks, hist_window, chunk_tokens, n_heads, head_dim, stream,
-                       rope=None):
+                       rope=None, split=True):
     """A whole 1F1C rollout of one layer through wf_1f1c_plan / wf_1f1c_run_round: pipeline
     fill, steady state, drain. The null model's Q/K/V come from a device pool of seeded draws
     reused across chunks (timing only needs the shapes); each round is timed with events."""
@@ -403,7 +407,8 @@ def bench_rollout_1f1c(torch, wf, n_steps, n_chunks, hist_window, chunk_tokens, 
         return qblock[:plan.n_inflight * C], ks, vs
 
     scale = 1.0 / float(np.sqrt(D))
-    ro = wf.Rollout1F1C(n_steps, n_chunks, hist_window, C, H, D, scale, torch.bfloat16, stream=stream, rope=rope)
+    ro = wf.Rollout1F1C(n_steps, n_chunks, hist_window, C, H, D, scale, torch.bfloat16, stream=stream, rope=rope,
+                        split=split)
     timers, plans = [], []
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -438,7 +443,7 @@ def bench_rollout_1f1c(torch, wf, n_steps, n_chunks, hist_window, chunk_tokens, 
     return res
 
 
-def bench_power(torch, wf, cfg, seconds):
+def bench_power(torch, wf, cfg, seconds, split=True):
     """Board power while the headline attention runs back to back, and energy per launch."""
     from chunk_causal_dit_amd.profiling import sample_power
     C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
@@ -450,11 +455,12 @@ def bench_power(torch, wf, cfg, seconds):
         for c in range(n):
             cache.append(kk[c * C:(c + 1) * C], vv[c * C:(c + 1) * C])
     out = torch.empty_like(q)
+    ws = wf.attn_fwd_workspace(cache) if split else None
     reps = 20
 
     def run():
         for _ in range(reps):
-            wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, with_lse=False)
+            wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, out=out, with_lse=False, workspace=ws)
 
     run()
     torch.cuda.synchronize()
@@ -489,6 +495,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the rollout, int8-QK, W8A8 and 1F1C rollout measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0, help="run a plain copy of this size first")
+    ap.add_argument("--no-split", action="store_true",
+                    help="time wf_chunk_causal_attn_fwd (no key split of chunk 0) instead of the workspace call")
     ap.add_argument("--w8a8-only", action="store_true",
                     help="run only the W8A8 linear measurement and print its JSON (for profiling)")
     ap.add_argument("--rollout-only", action="store_true",
@@ -517,15 +525,17 @@ def main():
         copy_probe(torch, args.copy_probe_mib)
 
     cfg = CONFIGS["wan13b_4step"]
+    split = not args.no_split
     if args.w8a8_only:
         print(json.dumps({"w8a8": bench_w8a8(torch, wf, cfg.nq, args.steps, args.warmup, stream)}), flush=True)
         return
     if args.rollout_only:
         print(json.dumps({"rollout_1f1c": {
-            "4step": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream)}}),
+            "4step": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream,
+                                        split=split)}}),
             flush=True)
         return
-    inp, ms_per_step, kv_ms, attn_ms = bench_round(torch, wf, cfg, args.steps, args.warmup, stream)
+    inp, ms_per_step, kv_ms, attn_ms = bench_round(torch, wf, cfg, args.steps, args.warmup, stream, split=split)
     print(f"[bench] {cfg.name}: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     eff = effective_flops(cfg)
@@ -567,21 +577,25 @@ def main():
                       "frac_of_hbm_peak": kv_bytes / (np.median(kv_ms) / 1e3) / 1e9 / HBM_GBS},
         "roofline": {
             "bound": "mfma",
-            "kernel": ATTN_KERNEL,
+            "kernel": ATTN_KERNEL + (" + " + MERGE_KERNEL if split else ""),
+            "call": "wf_chunk_causal_attn_fwd_ws (key split of in-flight chunk 0)" if split
+                    else "wf_chunk_causal_attn_fwd",
             "achieved": achieved,
             "peak": BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / BF16_DENSE_TFLOPS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": attention_min_bytes(cfg),
-            "timing": "hip events on the launch stream around each attention launch, mean over the timed steps",
+            "timing": "hip events on the launch stream around each attention call (the attention kernel, plus the "
+                      "merge kernel of the split), mean over the timed steps",
         },
     }
     if args.power_seconds > 0:
-        res["power"] = bench_power(torch, wf, cfg, args.power_seconds)
+        res["power"] = bench_power(torch, wf, cfg, args.power_seconds, split=split)
     if not args.no_extras:
-        res["rollout"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream)
-        res["rollout_fused"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream, fused=True)
+        res["rollout"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream, split=split)
+        res["rollout_fused"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream, fused=True,
+                                             split=split)
         print("[bench] rollout done", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         res["i8qk"] = bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], 20, 3, stream)
@@ -589,9 +603,12 @@ def main():
         res["w8a8"] = bench_w8a8(torch, wf, cfg.nq, 20, 3, stream)
         print("[bench] W8A8 linears done", file=sys.stderr, flush=True)
         res["rollout_1f1c"] = {
-            "4step": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream),
-            "5step": bench_rollout_1f1c(torch, wf, 5, 133, 3, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream),
+            "4step": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream,
+                                        split=split),
+            "5step": bench_rollout_1f1c(torch, wf, 5, 133, 3, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream,
+                                        split=split),
             "4step_rope": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream,
+                                             split=split,
                                              rope={"frames_per_chunk": 3, "grid_h": 30, "grid_w": 52}),
         }
         print("[bench] 1F1C rollouts done", file=sys.stderr, flush=True)

@@ -9,7 +9,8 @@ Calls mirror include/wf.h:
     KVCache(...)                 wf_kv_pool_bytes / wf_kv_cache_create
       .append / .refresh / .evict / .set_table / .table
     rope3d(x, ...)               wf_rope3d (in place)
-    chunk_causal_attn_fwd(...)   wf_chunk_causal_attn_fwd
+    chunk_causal_attn_fwd(...)   wf_chunk_causal_attn_fwd, or wf_chunk_causal_attn_fwd_ws
+                                 with a workspace (attn_fwd_workspace_bytes)
     chunk_causal_attn_fwd_i8qk(...), attn_i8qk_workspace_bytes(...)
 """
 from __future__ import annotations
@@ -24,7 +25,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 __all__ = [
     "WFError", "lib", "library_path", "exported_symbols", "header_symbols",
     "WF_F32", "WF_BF16", "KVCache", "kv_pool_bytes", "rope3d",
-    "chunk_causal_attn_fwd", "attn_i8qk_workspace_bytes", "chunk_causal_attn_fwd_i8qk",
+    "chunk_causal_attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_workspace", "attn_i8qk_workspace_bytes", "chunk_causal_attn_fwd_i8qk",
     "quant_rows_i8", "gemm_w8a8", "WF_I32",
     "WF_MAX_TABLE", "RoundPlan", "rounds_1f1c", "plan_1f1c", "run_round", "Rollout1F1C",
 ]
@@ -91,6 +92,8 @@ _SIGNATURES = {
     "wf_kv_get_table": (_c_int, [_vp, ctypes.POINTER(_c_int), _c_int, ctypes.POINTER(_c_int)]),
     "wf_rope3d": (_c_int, [_vp] + [_c_int] * 11 + [ctypes.c_float, _vp]),
     "wf_chunk_causal_attn_fwd": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp]),
+    "wf_attn_fwd_workspace_bytes": (_c_size, [_vp]),
+    "wf_chunk_causal_attn_fwd_ws": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp]),
     "wf_kv_set_rope": (_c_int, [_vp] + [_c_int] * 6 + [ctypes.c_float]),
     "wf_kv_append_rope": (_c_int, [_vp, _vp, _vp, _c_int, _vp, ctypes.POINTER(_c_int)]),
     "wf_kv_refresh_rope": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _vp]),
@@ -101,7 +104,7 @@ _SIGNATURES = {
     "wf_1f1c_rounds": (_c_int, [_c_int, _c_int]),
     "wf_1f1c_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(RoundPlan)]),
     "wf_1f1c_run_round": (_c_int, [_vp, ctypes.POINTER(RoundPlan), _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
-                                   ctypes.c_float, _vp, _vp, _vp]),
+                                   ctypes.c_float, _vp, _vp, _vp, _vp]),
     "wf_status_str": (ctypes.c_char_p, [_c_int]),
     "wf_last_error": (ctypes.c_char_p, []),
     "wf_version": (_c_int, []),
@@ -298,14 +301,32 @@ def _attn_io(q, cache, n_inflight, out, lse, with_lse):
     return out, lse
 
 
+def attn_fwd_workspace_bytes(cache: KVCache) -> int:
+    """Bytes of the key-split workspace of wf_chunk_causal_attn_fwd_ws (0 for fp32 caches)."""
+    return int(lib().wf_attn_fwd_workspace_bytes(cache.handle))
+
+
+def attn_fwd_workspace(cache: KVCache) -> Optional[torch.Tensor]:
+    """A device workspace for the key split of this cache's rounds, or None when it has none."""
+    n = attn_fwd_workspace_bytes(cache)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+
+
 def chunk_causal_attn_fwd(q: torch.Tensor, cache: KVCache, n_inflight: int, scale: float,
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          with_lse: bool = True, stream=None):
-    """Chunk-wise causal attention of the round. Returns (out, lse or None)."""
+                          with_lse: bool = True, stream=None, workspace: Optional[torch.Tensor] = None):
+    """Chunk-wise causal attention of the round. Returns (out, lse or None). With a workspace
+    (attn_fwd_workspace) it calls wf_chunk_causal_attn_fwd_ws, which may split chunk 0's keys."""
     out, lse = _attn_io(q, cache, n_inflight, out, lse, with_lse)
-    _check(lib().wf_chunk_causal_attn_fwd(_dev(q, "q"), cache.handle, n_inflight, float(scale), _dev(out, "out"),
-                                          _dev(lse, "lse") if lse is not None else None, _vp(_stream(stream))),
-           "wf_chunk_causal_attn_fwd")
+    lse_p = _dev(lse, "lse") if lse is not None else None
+    if workspace is None:
+        _check(lib().wf_chunk_causal_attn_fwd(_dev(q, "q"), cache.handle, n_inflight, float(scale),
+                                              _dev(out, "out"), lse_p, _vp(_stream(stream))),
+               "wf_chunk_causal_attn_fwd")
+    else:
+        _check(lib().wf_chunk_causal_attn_fwd_ws(_dev(q, "q"), cache.handle, n_inflight, float(scale),
+                                                 _dev(workspace, "workspace"), _dev(out, "out"), lse_p,
+                                                 _vp(_stream(stream))), "wf_chunk_causal_attn_fwd_ws")
     return out, lse
 
 
@@ -379,11 +400,13 @@ def plan_1f1c(n_steps: int, n_chunks: int, hist_window: int, r: int) -> RoundPla
 
 def run_round(cache: KVCache, plan: RoundPlan, q: torch.Tensor, ks: Sequence[torch.Tensor],
               vs: Sequence[torch.Tensor], scale: float, out: Optional[torch.Tensor] = None,
-              lse: Optional[torch.Tensor] = None, with_lse: bool = True, stream=None):
+              lse: Optional[torch.Tensor] = None, with_lse: bool = True, stream=None,
+              workspace: Optional[torch.Tensor] = None):
     """One round on the stream: append the new chunk, refresh the other in-flight entries,
     attention over the round's query block, evict. ks[i], vs[i] are this round's K/V of
     in-flight chunk i (cleanest first). With a RoPE geometry on the cache (set_rope), q is
-    rotated in place and K inside the cache writes. Returns (out, lse or None)."""
+    rotated in place and K inside the cache writes. A workspace (attn_fwd_workspace) lets the
+    attention split chunk 0's keys. Returns (out, lse or None)."""
     N = plan.n_inflight
     if len(ks) != N or len(vs) != N:
         raise ValueError(f"need {N} K and V chunks, got {len(ks)} and {len(vs)}")
@@ -391,6 +414,7 @@ def run_round(cache: KVCache, plan: RoundPlan, q: torch.Tensor, ks: Sequence[tor
     kp = (_vp * N)(*[cache._chunk(t, "k").value for t in ks])
     vp = (_vp * N)(*[cache._chunk(t, "v").value for t in vs])
     _check(lib().wf_1f1c_run_round(cache.handle, ctypes.byref(plan), _dev(q, "q"), kp, vp, float(scale),
+                                   _dev(workspace, "workspace") if workspace is not None else None,
                                    _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
                                    _vp(_stream(stream))), "wf_1f1c_run_round")
     return out, lse
@@ -403,11 +427,12 @@ class Rollout1F1C:
     this round's K and V chunks of the in-flight chunks, cleanest first. Each call of
     step() plans the next round (wf_1f1c_plan) and enqueues it (wf_1f1c_run_round).
     With rope (the 3D geometry of wf_kv_set_rope), the query block is rotated in place
-    each round and K inside the cache writes, at the chunks' global indices."""
+    each round and K inside the cache writes, at the chunks' global indices. With split
+    (default), the rounds' attention runs with a key-split workspace held by the rollout."""
 
     def __init__(self, n_steps: int, n_chunks: int, hist_window: int, chunk_tokens: int, n_heads: int,
                  head_dim: int, scale: float, dtype: torch.dtype = torch.bfloat16, n_slots: Optional[int] = None,
-                 stream=None, rope: Optional[dict] = None):
+                 stream=None, rope: Optional[dict] = None, split: bool = True):
         self.n_steps, self.n_chunks, self.hist_window, self.scale = n_steps, n_chunks, hist_window, scale
         self.n_rounds = rounds_1f1c(n_steps, n_chunks)
         plan_1f1c(n_steps, n_chunks, hist_window, 0)  # validates the window
@@ -416,6 +441,7 @@ class Rollout1F1C:
         if rope is not None:  # {"frames_per_chunk", "grid_h", "grid_w", optional "split", "theta"}
             self.cache.set_rope(rope["frames_per_chunk"], rope["grid_h"], rope["grid_w"],
                                 tuple(rope.get("split", (44, 42, 42))), rope.get("theta", 10000.0))
+        self.workspace = attn_fwd_workspace(self.cache) if split else None
         self.round = 0
         self.stream = stream
 
@@ -425,6 +451,7 @@ class Rollout1F1C:
             raise StopIteration("the rollout is complete")
         plan = plan_1f1c(self.n_steps, self.n_chunks, self.hist_window, self.round)
         q, ks, vs = model(plan)
-        o, l = run_round(self.cache, plan, q, ks, vs, self.scale, out=out, with_lse=with_lse, stream=self.stream)
+        o, l = run_round(self.cache, plan, q, ks, vs, self.scale, out=out, with_lse=with_lse, stream=self.stream,
+                         workspace=self.workspace)
         self.round += 1
         return plan, o, l

@@ -106,6 +106,7 @@ __device__ __forceinline__ void pin_weights(bf16x8 (&p)[4]) {
 
 struct Work {
   int j, h, qt;
+  int part;  // -1, or the half (0, 1) of the key tiles of a split query tile
 };
 
 constexpr int kXcds = 8;  // workgroup i of a launch runs on XCD i % 8; each XCD has its own L2
@@ -134,6 +135,26 @@ __device__ __forceinline__ Work decode_block(int b, int N, int H, int T) {
   w.j = N - 1 - cls;
   w.h = rem / T;
   w.qt = rem - w.h * T;
+  w.part = -1;
+  return w;
+}
+
+// Work item of workgroup b when in-flight chunk 0 is split over its key tiles
+// (split = 2): chunks N-1 .. 1 first, in the order above; then the query tiles of
+// chunk 0 as 2H "heads" (head h, half p -> 2h + p) in the same XCD-run order, so the
+// short halves fill the end of the grid.
+__device__ __forceinline__ Work decode_work(int b, const wf::AttnParams& p) {
+  const int N = p.n_inflight, H = p.n_heads, T = p.q_tiles;
+  if (!p.split) return decode_block(b, N, H, T);
+  const int n_main = (N - 1) * H * T;
+  if (b < n_main) {
+    Work w = decode_block(b, N - 1, H, T);
+    w.j += 1;
+    return w;
+  }
+  Work w = decode_block(b - n_main, 1, 2 * H, T);
+  w.part = w.h & 1;
+  w.h >>= 1;
   return w;
 }
 
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
   constexpr int DB = D / 32;               // 32-row blocks of O^T
   char* smem = g_smem;
 
-  const Work w = decode_block(blockIdx.x, p.n_inflight, p.n_heads, p.q_tiles);
+  const Work w = decode_work(blockIdx.x, p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = (wave >> 2) ^ WF_ATTN_LEAD_GROUP;  // group 0 leads by half a step
@@ -245,7 +266,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
 
   const int ktc = p.key_tiles;
   const int n_vis = p.n_hist + w.j + 1;  // visible logical chunks
-  const int n_iter = n_vis * ktc;
+  // key tiles t_base .. t_base + n_iter - 1 of the visible ones (all of them, or one half)
+  const int n_all = n_vis * ktc;
+  const int t_base = w.part == 1 ? n_all / 2 : 0;
+  const int n_iter = w.part < 0 ? n_all : (w.part == 0 ? n_all / 2 : n_all - n_all / 2);
   const char* kpool = I8 ? reinterpret_cast<const char*>(p.k_codes) : static_cast<const char*>(p.k_pool);
   const char* vpool = static_cast<const char*>(p.v_pool);
   const size_t slot_bytes = (size_t)p.slot_elems * G::ES;
@@ -262,10 +286,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     c.voff = (size_t)p.slots[c.cl] * slot_bytes + head_off;
     c.koff = I8 ? ((size_t)c.cl * H + w.h) * kchunk_bytes : c.voff;
   };
-  auto cursor_at = [&](int t) {
+  auto cursor_at = [&](int t) {  // t counts from the first tile of this workgroup's range
     Cursor c;
-    c.cl = t / ktc;
-    c.kt = t - c.cl * ktc;
+    c.cl = (t_base + t) / ktc;
+    c.kt = (t_base + t) - c.cl * ktc;
     chunk_start(c);
     c.voff += (size_t)c.kt * TB::V;
     c.koff += (size_t)c.kt * TB::K;
@@ -490,7 +514,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     }
   } else if (!PINGPONG || grp == 0) {
     // in-phase order (and ping-pong group 0): M_t, [barrier], V_t, copies + barrier
-    int vkt = 0, vcl = 0;
+    int vkt = t_base % ktc, vcl = t_base / ktc;
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
       mblock(r);
       if (PINGPONG) {
@@ -509,7 +533,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     }
   } else {
     // ping-pong group 1, half a step behind: V_{t-1}, barrier, M_t, copies + barrier
-    int vkt = 0, vcl = 0;
+    int vkt = t_base % ktc, vcl = t_base / ktc;
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
       if (t >= 1) {
         vblock(vkt, vcl);
@@ -526,7 +550,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     }
   }
 
-  if (wave_on) {
+  if (wave_on && w.part >= 0) {  // one half of a split query tile: unnormalized partials
+    const float lt = halves_sum((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+    if (row_ok) {
+      const size_t pr = ((size_t)w.part * H + w.h) * C + row;  // chunk 0: row is the chunk row
+      float* orow = p.part_o + pr * D;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<f32x4*>(orow + 32 * d + 8 * a + 4 * hh) =
+              f32x4{o[d][4 * a], o[d][4 * a + 1], o[d][4 * a + 2], o[d][4 * a + 3]};
+      if (hh == 0) *reinterpret_cast<float2*>(p.part_ml + 2 * pr) = float2{m_ref, lt};
+    }
+  } else if (wave_on) {
     const float lt = halves_sum((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
     const float inv = 1.0f / lt;
     if (row_ok) {
@@ -696,6 +733,32 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32_kernel(wf::AttnParams p)
   }
 }
 
+// Merges the two halves of the split query tiles of chunk 0: one wave per (row, head).
+// With the halves' log2-domain maxima m0, m1 and weight sums l0, l1 (weights taken
+// against their own maxima): M = max, w_p = 2^(m_p - M), L = l0 w0 + l1 w1,
+// O = (O0 w0 + O1 w1) / L, LSE = (M + log2 L) ln 2.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(wf::AttnParams p) {
+  constexpr int PER = D / 64;  // dims per lane
+  const int C = p.chunk_tokens, H = p.n_heads;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wv >= C * H) return;
+  const int row = wv / H, h = wv - row * H;
+  const size_t r0 = (size_t)h * C + row, r1 = ((size_t)H + h) * C + row;
+  const float2 ml0 = *reinterpret_cast<const float2*>(p.part_ml + 2 * r0);
+  const float2 ml1 = *reinterpret_cast<const float2*>(p.part_ml + 2 * r1);
+  const float m = fmaxf(ml0.x, ml1.x);
+  const float w0 = fast_exp2(ml0.x - m), w1 = fast_exp2(ml1.x - m);
+  const float l = ml0.y * w0 + ml1.y * w1;
+  const float inv = 1.0f / l;
+  const float* o0 = p.part_o + r0 * D + lane * PER;
+  const float* o1 = p.part_o + r1 * D + lane * PER;
+  __bf16* out = static_cast<__bf16*>(p.o) + ((size_t)row * H + h) * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) out[e] = (__bf16)((o0[e] * w0 + o1[e] * w1) * inv);
+  if (p.lse && lane == 0) p.lse[(size_t)h * p.n_inflight * C + row] = (m + log2f(l)) * kLn2;
+}
+
 template <typename Kern>
 hipError_t launch(Kern k, int lds, int grid, int block, const wf::AttnParams& p, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -708,16 +771,40 @@ hipError_t launch(Kern k, int lds, int grid, int block, const wf::AttnParams& p,
 
 namespace wf {
 
-hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& p, hipStream_t s) {
+size_t attn_split_bytes(const wf_kv_cache& kv) {
+  if (kv.dtype != WF_BF16) return 0;
+  const size_t rows = (size_t)2 * kv.n_heads * kv.chunk_tokens;
+  return (rows * kv.head_dim * 4 + 255) / 256 * 256 + (rows * 8 + 255) / 256 * 256;
+}
+
+hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& p, void* workspace, hipStream_t s) {
   const int C = kv.chunk_tokens;
   p.key_tiles = (C + KT - 1) / KT;
   if (kv.dtype == WF_BF16) {
     constexpr int NW = 8;
     p.q_tiles = (C + NW * 32 - 1) / (NW * 32);
-    const int grid = p.n_inflight * kv.n_heads * p.q_tiles;
+    // Split chunk 0 (the shortest items) over its key tiles when there is a longer
+    // chunk class for its halves to fill in behind and at least two key tiles to halve.
+    p.split = workspace && p.n_inflight >= 2 && (long long)(p.n_hist + 1) * p.key_tiles >= 2;
+    if (p.split) {
+      const size_t rows = (size_t)2 * kv.n_heads * C;
+      p.part_o = static_cast<float*>(workspace);
+      p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + (rows * kv.head_dim * 4 + 255) / 256 * 256);
+    }
+    // a split chunk 0 runs as two workgroups per query tile
+    const int grid = (p.n_inflight + (p.split ? 1 : 0)) * kv.n_heads * p.q_tiles;
+    hipError_t e = kv.head_dim == 128
+                       ? launch(attn_fwd_bf16_kernel<128, NW, WF_ATTN_PINGPONG>, TileBytes<128, false>::LDS, grid,
+                                NW * 64, p, s)
+                       : launch(attn_fwd_bf16_kernel<64, NW, WF_ATTN_PINGPONG>, TileBytes<64, false>::LDS, grid,
+                                NW * 64, p, s);
+    if (e != hipSuccess || !p.split) return e;
+    const int blocks = (C * kv.n_heads + 3) / 4;  // one wave per (row, head) of chunk 0
     if (kv.head_dim == 128)
-      return launch(attn_fwd_bf16_kernel<128, NW, WF_ATTN_PINGPONG>, TileBytes<128, false>::LDS, grid, NW * 64, p, s);
-    return launch(attn_fwd_bf16_kernel<64, NW, WF_ATTN_PINGPONG>, TileBytes<64, false>::LDS, grid, NW * 64, p, s);
+      attn_combine_kernel<128><<<blocks, 256, 0, s>>>(p);
+    else
+      attn_combine_kernel<64><<<blocks, 256, 0, s>>>(p);
+    return hipGetLastError();
   }
   constexpr int NW = 4;
   p.q_tiles = (C + NW * 32 - 1) / (NW * 32);

@@ -64,7 +64,8 @@ WF_EXPORT int wf_1f1c_plan(int n_steps, int n_chunks, int hist_window, int round
 }
 
 WF_EXPORT int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void* q, const void* const* k,
-                                const void* const* v, float scale, void* out, float* lse, void* stream) {
+                                const void* const* v, float scale, void* workspace, void* out, float* lse,
+                                void* stream) {
   const char* who = "wf_1f1c_run_round";
   if (!kv || !plan || !q || !k || !v || !out) return fail(WF_E_NULL, "%s: NULL argument", who);
   const int N = plan->n_inflight, Hs = plan->n_hist;
@@ -85,6 +86,8 @@ WF_EXPORT int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void
   if (!aligned16(q) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return fail(WF_E_SHAPE, "%s: q and out must be 16-byte aligned, lse 4-byte aligned", who);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(WF_E_SHAPE, "%s: scale must be positive and finite", who);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(WF_E_SHAPE, "%s: workspace must be 256-byte aligned", who);
   if (append && kv->free_slots.empty()) return fail(WF_E_FULL, "%s: no free slot for the new chunk", who);
   if ((long long)N * kv->chunk_tokens * kv->n_heads * kv->head_dim >= (1LL << 40))
     return fail(WF_E_SHAPE, "%s: query block too large", who);
@@ -117,6 +120,6 @@ WF_EXPORT int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void
     for (int i = 0; i < N - (append ? 1 : 0); ++i)
       if ((st = wf_kv_refresh(kv, Hs + i, k[i], v[i], stream)) != WF_OK) return st;
   }
-  if ((st = wf_chunk_causal_attn_fwd(q, kv, N, scale, out, lse, stream)) != WF_OK) return st;
+  if ((st = wf_chunk_causal_attn_fwd_ws(q, kv, N, scale, workspace, out, lse, stream)) != WF_OK) return st;
   return wf_kv_evict(kv, plan->evict_after);
 }

@@ -300,7 +300,19 @@ WF_EXPORT int wf_chunk_causal_attn_fwd(const void* q, const wf_kv_cache* kv, int
   AttnParams p;
   int st = fill_attn_params(q, kv, n_inflight, scale, out, lse, p, "wf_chunk_causal_attn_fwd");
   if (st != WF_OK) return st;
-  return hip_status(launch_attn_fwd(*kv, p, static_cast<hipStream_t>(stream)), "wf_chunk_causal_attn_fwd");
+  return hip_status(launch_attn_fwd(*kv, p, nullptr, static_cast<hipStream_t>(stream)), "wf_chunk_causal_attn_fwd");
+}
+
+WF_EXPORT size_t wf_attn_fwd_workspace_bytes(const wf_kv_cache* kv) { return kv ? attn_split_bytes(*kv) : 0; }
+
+WF_EXPORT int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
+                                          void* workspace, void* out, float* lse, void* stream) {
+  const char* who = "wf_chunk_causal_attn_fwd_ws";
+  if (workspace && !aligned(workspace, 256)) return fail(WF_E_SHAPE, "%s: workspace must be 256-byte aligned", who);
+  AttnParams p;
+  int st = fill_attn_params(q, kv, n_inflight, scale, out, lse, p, who);
+  if (st != WF_OK) return st;
+  return hip_status(launch_attn_fwd(*kv, p, workspace, static_cast<hipStream_t>(stream)), who);
 }
 
 WF_EXPORT size_t wf_attn_i8qk_workspace_bytes(const wf_kv_cache* kv, int n_inflight) {

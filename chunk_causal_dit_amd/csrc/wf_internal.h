@@ -90,10 +90,20 @@ struct AttnParams {
   const float* k_scales;       // [H][n_tab][q_blocks]
   const float* qm;             // [H][N*C]
   int q_blocks;                // 128-token blocks per chunk
+  // Key-range split of in-flight chunk 0 (bf16 path): with split = 2 each of its query
+  // tiles runs as two workgroups over the two halves of its key tiles, which write
+  // unnormalized partials to part_o [2][H][C][D] and their log2-domain row max and
+  // weight sum to part_ml [2][H][C][2]; attn_combine_kernel merges them.
+  int split;
+  float* part_o;
+  float* part_ml;
   int slots[WF_MAX_TABLE];  // physical slot of logical chunk c = 0..n_hist+n_inflight-1
 };
 
-hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& prm, hipStream_t s);
+// workspace: NULL, or attn_split_bytes(kv) bytes (256-byte aligned) that enable the key split
+hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& prm, void* workspace, hipStream_t s);
+// Bytes of the key-split partials of a bf16 cache (0 for fp32 caches, which never split).
+size_t attn_split_bytes(const wf_kv_cache& kv);
 
 // ---- W8A8 linear ----
 hipError_t launch_quant_rows_i8(const void* x, int rows, int cols, void* q, float* scales, hipStream_t s);

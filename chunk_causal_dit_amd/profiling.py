@@ -2,13 +2,15 @@
 
     python -m chunk_causal_dit_amd.profiling stats  <run_kernel_stats.csv> --cmd "<command>" --out <file.md>
     python -m chunk_causal_dit_amd.profiling traffic --fetch <fetch counter_collection.csv>
-        --write <write counter_collection.csv> --kernel <name substring> --copy-bytes <bytes>
+        --write <write counter_collection.csv> --kernel <name substring> [--kernel <another> ...]
+        --copy-bytes <bytes>
         --cmd "<command>" --source <kernel .hip file> --out <file.json>
 
 ``stats`` turns a ``--kernel-trace --stats`` run into a short markdown table
 (calls, average / min / max duration per kernel). ``traffic`` turns two
 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs into HBM bytes per launch of
-one kernel. Both counters are read in KiB per dispatch; each is calibrated by
+one kernel, or per call of a group of kernels launched once each per call (the
+per-kernel figures are kept, and their sum is the call's). Both counters are read in KiB per dispatch; each is calibrated by
 what it reads for a plain device-to-device copy of known size in the same run
 (the largest dispatch whose name contains "copy"): factor = counter KiB * 1024
 / copy bytes, and the kernel's bytes = counter KiB * 1024 / factor. The JSON
@@ -138,7 +140,7 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, action="append")
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--source", required=True)
@@ -150,18 +152,24 @@ def main(argv=None):
         open(a.out, "w").write(text)
         print(text)
         return
-    fetch = calibrated_bytes(a.fetch, "FETCH_SIZE", a.kernel, a.copy_bytes)
-    write = calibrated_bytes(a.write, "WRITE_SIZE", a.kernel, a.copy_bytes)
+    per_kernel = {}
+    for k in a.kernel:
+        fetch = calibrated_bytes(a.fetch, "FETCH_SIZE", k, a.copy_bytes)
+        write = calibrated_bytes(a.write, "WRITE_SIZE", k, a.copy_bytes)
+        per_kernel[k] = {"fetch": fetch, "write": write,
+                         "hbm_bytes_per_launch": fetch["bytes_per_launch"] + write["bytes_per_launch"]}
     rec = {
-        "kernel": a.kernel,
+        "kernel": " + ".join(a.kernel),
         "command": a.cmd,
         "kernel_source_sha256_16": hashlib.sha256(open(a.source, "rb").read()).hexdigest()[:16],
         "copy_bytes": a.copy_bytes,
-        "fetch": fetch,
-        "write": write,
-        "hbm_bytes_per_launch": fetch["bytes_per_launch"] + write["bytes_per_launch"],
-        "algorithmic_bytes_per_launch": a.algorithmic_bytes,
     }
+    if len(a.kernel) == 1:
+        rec.update({"fetch": per_kernel[a.kernel[0]]["fetch"], "write": per_kernel[a.kernel[0]]["write"]})
+    else:
+        rec["per_kernel"] = per_kernel
+    rec["hbm_bytes_per_launch"] = sum(v["hbm_bytes_per_launch"] for v in per_kernel.values())
+    rec["algorithmic_bytes_per_launch"] = a.algorithmic_bytes
     json.dump(rec, open(a.out, "w"), indent=1)
     json.dump(rec, sys.stdout, indent=1)
     print()

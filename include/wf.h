@@ -188,6 +188,28 @@ int wf_kv_refresh_rope(wf_kv_cache* kv, int logical_idx, const void* k, const vo
 int wf_chunk_causal_attn_fwd(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
                              void* out, float* lse, void* stream);
 
+/* Same operation with a caller-owned workspace that lets a bf16 round run
+ * in-flight chunk 0 (the chunk that sees the fewest keys) as two halves of
+ * its key range, whose partial softmax sums a second kernel merges: the
+ * shortest work items are halved so they pack into the end of the grid.
+ * Used when workspace != NULL, n_inflight >= 2 and chunk 0 sees at least two
+ * 64-key tiles; otherwise this is wf_chunk_causal_attn_fwd. The merge changes
+ * the summation order of chunk 0's rows only (results stay deterministic and
+ * within the same tolerance of the exact values; other chunks' rows are
+ * bitwise those of wf_chunk_causal_attn_fwd).
+ * workspace: NULL, or device memory of wf_attn_fwd_workspace_bytes(kv) bytes,
+ * 256-byte aligned, caller-owned, not overlapping q/out/lse, overwritten by
+ * every call (one buffer serves every round of a cache); after a split call
+ * it holds f32 [2][H][C][D] unnormalized halves, then at the next multiple of
+ * 256 bytes f32 [2][H][C][2] their log2-domain row max and weight sum.
+ * Calls that share a workspace must be ordered on one stream.
+ * Errors: those of wf_chunk_causal_attn_fwd; WF_E_SHAPE for a misaligned
+ * workspace. */
+size_t wf_attn_fwd_workspace_bytes(const wf_kv_cache* kv); /* 0 for fp32 caches */
+
+int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
+                                void* workspace, void* out, float* lse, void* stream);
+
 /* ------------------------------------------------------------------------
  * int8-QK variant (bf16 caches, head_dim 128). The pages name a
  * quantized-QK attention backend (SageAttention) in their DiT-only tests
@@ -289,8 +311,9 @@ int wf_1f1c_plan(int n_steps, int n_chunks, int hist_window, int round, wf_round
  * K/V (k[n_inflight-1], v[n_inflight-1]) when plan->new_chunk >= 0; refresh
  * every other in-flight entry i with k[i], v[i] (this round's K/V of that
  * chunk, [chunk_tokens][n_heads][head_dim] each, 16-byte aligned); run
- * wf_chunk_causal_attn_fwd over the n_inflight chunks (q, out: the round's
- * query block [n_inflight*chunk_tokens][n_heads][head_dim]; lse optional);
+ * wf_chunk_causal_attn_fwd_ws over the n_inflight chunks (q, out: the round's
+ * query block [n_inflight*chunk_tokens][n_heads][head_dim]; lse optional;
+ * workspace NULL or of wf_attn_fwd_workspace_bytes(kv) bytes, 256-aligned);
  * evict plan->evict_after oldest entries. The cache table must hold the
  * previous round's state: n_hist + n_inflight entries, less one when a chunk
  * is appended. k and v are host arrays of n_inflight device pointers.
@@ -302,7 +325,8 @@ int wf_1f1c_plan(int n_steps, int n_chunks, int hist_window, int round, wf_round
  * WF_E_SHAPE, WF_E_FULL; the cache is unchanged on these); WF_E_HIP means a
  * launch was rejected after earlier steps of the round were enqueued. */
 int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void* q, const void* const* k,
-                      const void* const* v, float scale, void* out, float* lse, void* stream);
+                      const void* const* v, float scale, void* workspace, void* out, float* lse,
+                      void* stream);
 
 /* ---- diagnostics ---- */
 const char* wf_status_str(int status); /* static string for a status code      */

@@ -67,14 +67,26 @@ def build_cache(wf, C, H, D, dtype, k_hist, v_hist, k_in, v_in, n_slots=None, ta
     return cache
 
 
-def gpu_round(wf, inp, table=None, n_slots=None, with_lse=True):
+def split_workspace(wf, cache):
+    """The key-split workspace of the cache, filled with NaN bytes so that a read of
+    anything the kernels did not write shows in the result."""
+    ws = wf.attn_fwd_workspace(cache)
+    if ws is not None:
+        ws.fill_(0xFF)
+    return ws
+
+
+def gpu_round(wf, inp, table=None, n_slots=None, with_lse=True, split=False):
+    """One round through the C ABI; split=True calls the workspace entry (key split of chunk 0)."""
     cfg = inp.cfg
     dt = torch_dtype(cfg.dtype)
     C, H, D = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim
     dev = {k: to_dev(getattr(inp, k), dt) for k in ("q", "k_hist", "v_hist", "k_in", "v_in")}
     cache = build_cache(wf, C, H, D, dt, dev["k_hist"], dev["v_hist"], dev["k_in"], dev["v_in"],
                         n_slots=n_slots, table=table)
-    out, lse = wf.chunk_causal_attn_fwd(dev["q"], cache, cfg.n_inflight, cfg.scale, with_lse=with_lse)
+    ws = split_workspace(wf, cache) if split else None
+    out, lse = wf.chunk_causal_attn_fwd(dev["q"], cache, cfg.n_inflight, cfg.scale, with_lse=with_lse,
+                                        workspace=ws)
     torch.cuda.synchronize()
     return out, lse, cache
 

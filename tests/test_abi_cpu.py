@@ -54,7 +54,7 @@ def test_exports_match_header(L):
     declared = wf.header_symbols()
     exported = wf.exported_symbols()
     assert declared == exported, (sorted(set(declared) - set(exported)), sorted(set(exported) - set(declared)))
-    assert len(declared) == 23
+    assert len(declared) == 25
 
 
 def test_version_and_status_strings(L):
@@ -162,8 +162,17 @@ def test_attention_argument_errors(L):
     assert f(ctypes.c_void_p(q.value + 2), h, 2, 0.1, q, None, None) == WF_E_SHAPE
     bad_lse = ctypes.cast(ctypes.c_void_p(pools.v.value + 2), ctypes.POINTER(ctypes.c_float))
     assert f(q, h, 2, 0.1, q, bad_lse, None) == WF_E_SHAPE
-    # the int8 variant: needs bf16 and head_dim 128
+    # the workspace variant: same checks, plus a 256-byte aligned workspace (NULL allowed)
+    fw = L.wf_chunk_causal_attn_fwd_ws
     ws = ctypes.c_void_p(pools.v.value)
+    assert fw(None, h, 2, 0.1, ws, q, None, None) == WF_E_NULL
+    assert fw(q, h, 4, 0.1, ws, q, None, None) == WF_E_EMPTY
+    assert fw(q, h, 2, 0.0, None, q, None, None) == WF_E_SHAPE
+    assert fw(q, h, 2, 0.1, ctypes.c_void_p(ws.value + 64), q, None, None) == WF_E_SHAPE
+    # bf16 cache, H=2, C=64 (make_cache defaults), D=64: 2 halves x H x C rows of D fp32 + (max, sum)
+    assert L.wf_attn_fwd_workspace_bytes(h) == 2 * 2 * 64 * 64 * 4 + 2 * 2 * 64 * 8
+    assert L.wf_attn_fwd_workspace_bytes(None) == 0
+    # the int8 variant: needs bf16 and head_dim 128
     g = L.wf_chunk_causal_attn_fwd_i8qk
     assert g(q, h, 2, 0.1, None, q, lse, None) == WF_E_NULL
     assert g(q, h, 2, 0.1, ws, q, lse, None) == WF_E_UNSUPPORTED  # head_dim 64
@@ -171,6 +180,7 @@ def test_attention_argument_errors(L):
     L.wf_kv_cache_destroy(h)
     h32, p32 = make_cache(L, n_slots=4, D=128, dtype=wf.WF_F32)
     assert g(q, h32, 2, 0.1, ws, q, lse, None) == WF_E_DTYPE
+    assert L.wf_attn_fwd_workspace_bytes(h32) == 0  # fp32 rounds never split
     L.wf_kv_cache_destroy(h32)
 
 

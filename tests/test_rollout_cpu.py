@@ -65,21 +65,23 @@ def test_run_round_refuses_before_enqueuing(L):
     plan = wf.plan_1f1c(4, 6, 2, 1)  # expects 1 entry held before the round (chunk 0), appends chunk 1
     ptrs = (ctypes.c_void_p * 2)(a.value, a.value)
     run = L.wf_1f1c_run_round
-    assert run(None, ctypes.byref(plan), a, ptrs, ptrs, 0.1, a, None, None) == WF_E_NULL
-    assert run(h, None, a, ptrs, ptrs, 0.1, a, None, None) == WF_E_NULL
-    assert run(h, ctypes.byref(plan), a, ptrs, ptrs, 0.1, a, None, None) == WF_E_SHAPE  # table empty, 1 expected
+    assert run(None, ctypes.byref(plan), a, ptrs, ptrs, 0.1, None, a, None, None) == WF_E_NULL
+    assert run(h, None, a, ptrs, ptrs, 0.1, None, a, None, None) == WF_E_NULL
+    assert run(h, ctypes.byref(plan), a, ptrs, ptrs, 0.1, None, a, None, None) == WF_E_SHAPE  # table empty, 1 expected
     assert table(L, h) == []
     plan0 = wf.plan_1f1c(4, 6, 2, 0)
     bad = (ctypes.c_void_p * 1)(a.value + 8)
-    assert run(h, ctypes.byref(plan0), a, bad, bad, 0.1, a, None, None) == WF_E_SHAPE  # misaligned K/V
+    assert run(h, ctypes.byref(plan0), a, bad, bad, 0.1, None, a, None, None) == WF_E_SHAPE  # misaligned K/V
     nul = (ctypes.c_void_p * 1)(None)
-    assert run(h, ctypes.byref(plan0), a, nul, nul, 0.1, a, None, None) == WF_E_NULL
+    assert run(h, ctypes.byref(plan0), a, nul, nul, 0.1, None, a, None, None) == WF_E_NULL
     one = (ctypes.c_void_p * 1)(a.value)
-    assert run(h, ctypes.byref(plan0), a, one, one, 0.0, a, None, None) == WF_E_SHAPE  # scale
-    assert run(h, ctypes.byref(plan0), ctypes.c_void_p(a.value + 4), one, one, 0.1, a, None, None) == WF_E_SHAPE
+    assert run(h, ctypes.byref(plan0), a, one, one, 0.0, None, a, None, None) == WF_E_SHAPE  # scale
+    assert run(h, ctypes.byref(plan0), ctypes.c_void_p(a.value + 4), one, one, 0.1, None, a, None, None) == WF_E_SHAPE
+    wsb = ctypes.c_void_p(a.value + 128)  # workspace not 256-byte aligned
+    assert run(h, ctypes.byref(plan0), a, one, one, 0.1, wsb, a, None, None) == WF_E_SHAPE
     forged = wf.plan_1f1c(4, 6, 2, 0)
     forged.evict_after = 5
-    assert run(h, ctypes.byref(forged), a, one, one, 0.1, a, None, None) == WF_E_SHAPE
+    assert run(h, ctypes.byref(forged), a, one, one, 0.1, None, a, None, None) == WF_E_SHAPE
     assert table(L, h) == []
     L.wf_kv_cache_destroy(h)
 
@@ -92,7 +94,7 @@ def test_run_round_full_cache(L):
     assert L.wf_kv_set_table(h, arr, 1) == WF_OK  # the one slot holds chunk 0
     plan = wf.plan_1f1c(4, 6, 2, 1)
     ptrs = (ctypes.c_void_p * 2)(a.value, a.value)
-    assert L.wf_1f1c_run_round(h, ctypes.byref(plan), a, ptrs, ptrs, 0.1, a, None, None) == WF_E_FULL
+    assert L.wf_1f1c_run_round(h, ctypes.byref(plan), a, ptrs, ptrs, 0.1, None, a, None, None) == WF_E_FULL
     assert table(L, h) == [0]
     L.wf_kv_cache_destroy(h)
 
@@ -106,12 +108,12 @@ def test_run_round_rope_checks(L):
     one = (ctypes.c_void_p * 1)(a.value)
     plan = wf.plan_1f1c(4, 6, 2, 0)
     plan.inflight_chunk[0] = 1 << 24  # frame position 2^24 and beyond: not exact in fp32
-    assert L.wf_1f1c_run_round(h, ctypes.byref(plan), a, one, one, 0.1, a, None, None) == WF_E_SHAPE
+    assert L.wf_1f1c_run_round(h, ctypes.byref(plan), a, one, one, 0.1, None, a, None, None) == WF_E_SHAPE
     arr = (ctypes.c_int * 1)(0)
     assert L.wf_kv_set_table(h, arr, 1) == WF_OK
     plan1 = wf.plan_1f1c(4, 6, 2, 1)  # chunks 0, 1 in flight
     plan1.inflight_chunk[1] = 5  # not consecutive
     two = (ctypes.c_void_p * 2)(a.value, a.value)
-    assert L.wf_1f1c_run_round(h, ctypes.byref(plan1), a, two, two, 0.1, a, None, None) == WF_E_SHAPE
+    assert L.wf_1f1c_run_round(h, ctypes.byref(plan1), a, two, two, 0.1, None, a, None, None) == WF_E_SHAPE
     assert table(L, h) == [0]
     L.wf_kv_cache_destroy(h)
