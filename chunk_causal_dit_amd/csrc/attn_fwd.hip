@@ -47,6 +47,7 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 constexpr int KT = 64;  // keys per tile
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kTileSumMax = 256.0f;  // 2^kRescaleLog2
 
 // A-operand row i of a 32-key block reads key key_of_arow(i). With the 32x32
 // output layout (lane half hh, element r <-> row 8*(r/4) + 4*hh + r%4) this
@@ -227,6 +228,10 @@ extern __shared__ __attribute__((aligned(1024))) char g_smem[];
 #endif
 #ifndef WF_ATTN_LEAD_GROUP
 #define WF_ATTN_LEAD_GROUP 1
+#endif
+// 1: the softmax skips the row max while the weights stay bounded (see vblock)
+#ifndef WF_ATTN_MAXFREE
+#define WF_ATTN_MAXFREE 1
 #endif
 
 // I8 = true: the int8-QK variant. S^T = K'^T Q^T runs on int8 MFMA over the
@@ -447,40 +452,67 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
         for (int e = 0; e < 16; ++e)
           if (32 * b + key_of_elem(hh, e) >= valid) s[b][e] = -INFINITY;
     }
-    // row max as four independent chains, then the other half of the row
-    float m4[4];
+    // Exact row max of the tile (four independent chains, then the other half of
+    // the row) and the lazy move of the reference max: the running output and
+    // sums are rescaled only when the tile max exceeds m_ref by kRescaleLog2.
+    auto move_max = [&](bool always) {
+      float m4[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      m4[c] = fmaxf(s[c >> 1][(c & 1) * 8], s[c >> 1][(c & 1) * 8 + 1]);
+      for (int c = 0; c < 4; ++c) {
+        m4[c] = fmaxf(s[c >> 1][(c & 1) * 8], s[c >> 1][(c & 1) * 8 + 1]);
 #pragma unroll
-      for (int e = 2; e < 8; ++e) m4[c] = fmaxf(m4[c], s[c >> 1][(c & 1) * 8 + e]);
-    }
-    float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-    const float tmax = mx * ct;
-    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleLog2)) {
-      const float mn = fmaxf(m_ref, tmax);
-      const float alpha = fast_exp2(m_ref - mn);
-      m_ref = mn;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) lsum[c] *= alpha;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-    }
-    const float nm = -m_ref;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) pk[2 * b + (e >> 3)][e & 7] = (__bf16)fast_exp2(fmaf(s[b][e], ct, nm));
-    // row sum of the weights actually used (bf16-rounded), four accumulators
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {pk[kk][2 * e], pk[kk][2 * e + 1]};
-        lsum[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[kk], false);
+        for (int e = 2; e < 8; ++e) m4[c] = fmaxf(m4[c], s[c >> 1][(c & 1) * 8 + e]);
       }
+      float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      const float tmax = mx * ct;
+      if (always || __builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleLog2)) {
+        const float mn = fmaxf(m_ref, tmax);
+        const float alpha = fast_exp2(m_ref - mn);
+        m_ref = mn;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lsum[c] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+      }
+    };
+    // weights 2^(s ct - m_ref) rounded to bf16, and this lane's share of their sum
+    // (the rounded weights actually used) in four accumulators
+    auto weights = [&](float (&ts)[4]) {
+      const float nm = -m_ref;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pk[2 * b + (e >> 3)][e & 7] = (__bf16)fast_exp2(fmaf(s[b][e], ct, nm));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        ts[kk] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 pr = {pk[kk][2 * e], pk[kk][2 * e + 1]};
+          ts[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ts[kk], false);
+        }
+      }
+    };
+    float ts[4];
+    if constexpr (WF_ATTN_MAXFREE) {
+      // Max-free fast path: weights against the current reference max. A lane's
+      // 32 weights summing to at most 2^kRescaleLog2 bound every weight by it, as
+      // the lazy move above would; a larger, infinite or NaN sum (the first tile,
+      // where m_ref = -inf, or a tile whose max moved up) takes the exact path.
+      weights(ts);
+      const float tl = (ts[0] + ts[1]) + (ts[2] + ts[3]);
+      if (__builtin_amdgcn_ballot_w64(!(tl <= kTileSumMax))) {
+        move_max(true);
+        weights(ts);
+      }
+    } else {
+      move_max(false);
+      weights(ts);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) lsum[kk] += ts[kk];
     if (WF_ATTN_SETPRIO == 2) __builtin_amdgcn_s_setprio(0);
   };
 
