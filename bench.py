@@ -540,6 +540,12 @@ def main():
 
     eff = effective_flops(cfg)
     attn_s = float(np.mean(attn_ms)) / 1e3
+    # the published dense peak, and the same figure from this device's CU count and peak clock
+    n_cu, clk_khz = wf.device_peak_info(torch.cuda.current_device())
+    peak_note = {"published_bf16_dense_tflops": BF16_DENSE_TFLOPS, "device_cus": n_cu,
+                 "device_peak_clock_mhz": clk_khz / 1e3,
+                 "derived_bf16_dense_tflops": n_cu * 4096 * clk_khz * 1e3 / 1e12,
+                 "used": "published"}
     achieved = eff / attn_s / 1e12
     kv_bytes = 4 * cfg.n_inflight * chunk_bytes(cfg)
     traffic = load_traffic(cfg.name)
@@ -575,6 +581,7 @@ def main():
         "kv_writes": {**ms_summary(kv_ms), "bytes": kv_bytes,
                       "gbs_median": kv_bytes / (np.median(kv_ms) / 1e3) / 1e9,
                       "frac_of_hbm_peak": kv_bytes / (np.median(kv_ms) / 1e3) / 1e9 / HBM_GBS},
+        "peak_note": peak_note,
         "roofline": {
             "bound": "mfma",
             "kernel": ATTN_KERNEL + (" + " + MERGE_KERNEL if split else ""),

@@ -27,7 +27,7 @@ __all__ = [
     "WF_F32", "WF_BF16", "KVCache", "kv_pool_bytes", "rope3d",
     "chunk_causal_attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_workspace", "attn_i8qk_workspace_bytes", "chunk_causal_attn_fwd_i8qk",
     "quant_rows_i8", "gemm_w8a8", "WF_I32",
-    "WF_MAX_TABLE", "RoundPlan", "rounds_1f1c", "plan_1f1c", "run_round", "Rollout1F1C",
+    "WF_MAX_TABLE", "RoundPlan", "device_peak_info", "rounds_1f1c", "plan_1f1c", "run_round", "Rollout1F1C",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +108,7 @@ _SIGNATURES = {
     "wf_status_str": (ctypes.c_char_p, [_c_int]),
     "wf_last_error": (ctypes.c_char_p, []),
     "wf_version": (_c_int, []),
+    "wf_device_peak_info": (_c_int, [_c_int, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
 }
 
 _lib = None
@@ -381,6 +382,13 @@ def gemm_w8a8(xq: torch.Tensor, sx: Optional[torch.Tensor], wq: torch.Tensor, sw
                               _dev(bias, "bias") if bias is not None else None, M, N, K, code, _dev(out, "out"),
                               _vp(_stream(stream))), "wf_gemm_w8a8")
     return out
+
+
+def device_peak_info(device: int = 0) -> Tuple[int, int]:
+    """(compute units, peak shader clock in kHz) of a device, as the HIP runtime reports them."""
+    cu, clk = _c_int(), _c_int()
+    _check(lib().wf_device_peak_info(device, ctypes.byref(cu), ctypes.byref(clk)), "wf_device_peak_info")
+    return cu.value, clk.value
 
 
 def rounds_1f1c(n_steps: int, n_chunks: int) -> int:

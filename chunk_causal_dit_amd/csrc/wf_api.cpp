@@ -388,3 +388,11 @@ WF_EXPORT const char* wf_status_str(int status) {
 WF_EXPORT const char* wf_last_error(void) { return g_last_error.c_str(); }
 
 WF_EXPORT int wf_version(void) { return 100; }  // 0.1.0
+
+WF_EXPORT int wf_device_peak_info(int device, int* n_cu, int* peak_clock_khz) {
+  const char* who = "wf_device_peak_info";
+  if (!n_cu || !peak_clock_khz) return fail(WF_E_NULL, "%s: NULL argument", who);
+  hipError_t e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(peak_clock_khz, hipDeviceAttributeClockRate, device);
+  return hip_status(e, who);
+}

@@ -332,6 +332,10 @@ int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void* q, const
 const char* wf_status_str(int status); /* static string for a status code      */
 const char* wf_last_error(void);      /* thread-local text of the last failure */
 int wf_version(void);                 /* major*10000 + minor*100 + patch       */
+/* Compute units and peak shader clock (kHz) of a device, as the runtime reports
+ * them: the dense bf16 MFMA peak is n_cu x 4096 flop/clk x clock. Host only,
+ * no device work; WF_E_NULL, or WF_E_HIP for an invalid device. */
+int wf_device_peak_info(int device, int* n_cu, int* peak_clock_khz);
 
 #ifdef __cplusplus
 }

@@ -54,7 +54,13 @@ def test_exports_match_header(L):
     declared = wf.header_symbols()
     exported = wf.exported_symbols()
     assert declared == exported, (sorted(set(declared) - set(exported)), sorted(set(exported) - set(declared)))
-    assert len(declared) == 25
+    assert len(declared) == 26
+
+
+def test_device_peak_info_argument_errors(L):
+    n = ctypes.c_int()
+    assert L.wf_device_peak_info(0, None, ctypes.byref(n)) == WF_E_NULL
+    assert L.wf_device_peak_info(0, ctypes.byref(n), None) == WF_E_NULL
 
 
 def test_version_and_status_strings(L):
