@@ -90,7 +90,7 @@ struct AttnParams {
   const float* k_scales;       // [H][n_tab][q_blocks]
   const float* qm;             // [H][N*C]
   int q_blocks;                // 128-token blocks per chunk
-  // Key-range split of in-flight chunk 0 (bf16 path): with split = 2 each of its query
+  // Key-range split of in-flight chunk 0 (bf16 path): with split set, each of its query
   // tiles runs as two workgroups over the two halves of its key tiles, which write
   // unnormalized partials to part_o [2][H][C][D] and their log2-domain row max and
   // weight sum to part_ml [2][H][C][2]; attn_combine_kernel merges them.
