@@ -109,10 +109,12 @@ def test_step5_round_refresh_overwrites_stale_slot():
     for j in range(1, N):
         cache.append(ki[j * C:(j + 1) * C], vi[j * C:(j + 1) * C])
     cache.refresh(Hs, ki[:C], vi[:C])  # this round's K/V of the refresh chunk
-    out, lse = wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale)
+    outs = {"whole": wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale),
+            "split": wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, workspace=RL.split_workspace(wf, cache))}
     torch.cuda.synchronize()
     rows = RL.boundary_rows(C, N, 8, seed=3)
     ref_o, ref_l = RL.oracle_round(inp, rows=rows)
-    got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
-    RL.assert_close(got, ref_o, "bf16", f"O ({len(rows)} rows)")
-    assert np.abs(lse.cpu().numpy()[:, rows] - ref_l).max() <= 2e-3
+    for name, (out, lse) in outs.items():
+        got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+        RL.assert_close(got, ref_o, "bf16", f"O ({len(rows)} rows, {name})")
+        assert np.abs(lse.cpu().numpy()[:, rows] - ref_l).max() <= 2e-3, name

@@ -1,8 +1,10 @@
 """Long rollout: 20 consecutive rounds over a 6-chunk history window kept in
 12 ring slots placed by a seeded permutation, with 3D RoPE on the in-flight
 queries and keys, append of the new chunk, refresh of the continuing chunks,
-attention and eviction each round. Compared with the plain-list ring model of
-the oracle: sampled rows every round, every row at rounds 0 and 19."""
+attention and eviction each round. Attention runs twice a round: with the
+key-split workspace (chunk 0's key range in two halves, then the merge) and
+without it. Both are compared with the plain-list ring model of the oracle:
+sampled rows every round, every row at rounds 0 and 19."""
 import os
 
 import numpy as np
@@ -31,6 +33,8 @@ def test_long_rollout_20_rounds():
     k0, v0 = make_rollout_init(cfg)
     n0 = Hs + N - 1
     cache = wf.KVCache(cfg.slots, C, H, D, dt)
+    ws = RL.split_workspace(wf, cache)
+    assert ws is not None
     cache.set_table(slot_permutation(cfg.slots, seed=cfg.seed)[:n0])
     ring = RingModel()
     kd, vd = RL.to_dev(k0, dt), RL.to_dev(v0, dt)
@@ -49,7 +53,8 @@ def test_long_rollout_20_rounds():
         cache.append(kd[(N - 1) * C:], vd[(N - 1) * C:])
         for j in range(N - 1):
             cache.refresh(Hs + j, kd[j * C:(j + 1) * C], vd[j * C:(j + 1) * C])
-        out, lse = wf.chunk_causal_attn_fwd(qd, cache, N, cfg.scale)
+        outs = {"split": wf.chunk_causal_attn_fwd(qd, cache, N, cfg.scale, workspace=ws),
+                "whole": wf.chunk_causal_attn_fwd(qd, cache, N, cfg.scale)}
         torch.cuda.synchronize()
         table = cache.table()
         assert len(table) == Hs + N and len(set(table)) == Hs + N
@@ -70,9 +75,10 @@ def test_long_rollout_20_rounds():
             qfull = np.zeros((N * C, H, D))
             qfull[rows] = qr
             ref_o, ref_l = OA.chunk_causal_attention(qfull, kvis, vvis, Hs, C, cfg.scale, rows=rows, workers=workers)
-        got = out.float().cpu().numpy() if full else out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
         print(f"[case] rollout round {r} ({'all' if full else len(rows)} rows), table {table}", flush=True)
-        RL.assert_close(got, ref_o, "bf16", f"round {r} O")
-        got_l = lse.cpu().numpy() if full else lse.cpu().numpy()[:, rows]
-        assert np.abs(got_l - ref_l).max() <= 5e-3
+        for name, (out, lse) in outs.items():
+            got = out.float().cpu().numpy() if full else out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+            RL.assert_close(got, ref_o, "bf16", f"round {r} O ({name})")
+            got_l = lse.cpu().numpy() if full else lse.cpu().numpy()[:, rows]
+            assert np.abs(got_l - ref_l).max() <= 5e-3, name
         ring.evict(1)
