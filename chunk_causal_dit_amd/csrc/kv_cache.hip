@@ -20,10 +20,12 @@
 // The fused write (append/refresh with RoPE) rotates K on its way into the
 // slot, so rotated K never makes a round trip through HBM. One workgroup
 // handles a slice of 256 / (pieces per row) tokens (16 for bf16 at head_dim
-// 128) of one head: each thread loads one 16-byte piece of K and of V,
-// rotates the K pairs (its own sin/cos), and the slice is written through LDS
-// as that key range of the tile images. Many small workgroups keep enough
-// loads in flight; the sin/cos work overlaps the memory latency.
+// 128) of a group of kRopeHeads heads: each thread owns one 16-byte piece
+// position of a token row, starts the loads of that piece of K and V for
+// every head of the group, computes the sin/cos of its pairs once (the angle
+// depends on the token and the pair, not on the head), rotates each head's K
+// pairs with them, and the slice is written through LDS as that key range of
+// the tile images of each head.
 #include "rope_common.h"
 
 namespace {
@@ -89,6 +91,11 @@ __global__ __launch_bounds__(256) void kv_tile_kernel(const T* __restrict__ ksrc
   }
 }
 
+#ifndef WF_ROPE_HEADS
+#define WF_ROPE_HEADS 4
+#endif
+constexpr int kRopeHeads = WF_ROPE_HEADS;  // heads per workgroup of the fused write
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void kv_rope_tile_kernel(const T* __restrict__ ksrc, const T* __restrict__ vsrc,
                                                            char* __restrict__ kdst, char* __restrict__ vdst, int C,
@@ -98,56 +105,72 @@ __global__ __launch_bounds__(256) void kv_rope_tile_kernel(const T* __restrict__
   constexpr int PPR = D / E;           // pieces per token row
   constexpr int TG = 256 / PPR;        // tokens per workgroup: one piece per thread
   constexpr int PAIRS = E / 2;         // rotated pairs per piece
+  constexpr int HG = kRopeHeads;
   constexpr int KROW = PPR * 16 + 16;  // LDS row pitch (bytes) of the K slice
   constexpr int VROW = D + 2;          // LDS row pitch (elements) of the V slice
   constexpr int TILE = 64 * D * (int)sizeof(T);
   static_assert(TG * PPR == 256 && 64 % TG == 0 && TG % E == 0, "tile slices must split evenly");
-  __shared__ __attribute__((aligned(16))) char kt[TG * KROW];
-  __shared__ T vt[TG][VROW];
-  const int t0 = blockIdx.x * TG, h = blockIdx.y;
+  __shared__ __attribute__((aligned(16))) char kt[HG][TG * KROW];
+  __shared__ T vt[HG][TG][VROW];
+  const int t0 = blockIdx.x * TG, h0 = blockIdx.y * HG;
   const int tile = t0 / 64, key0 = t0 % 64;
   const int tid = threadIdx.x;
-  {  // load, rotate, stage: thread (row r, piece c)
+  {  // load, rotate, stage: thread (row r, piece c) of every head of the group
     const int r = tid / PPR, c = tid % PPR;
     const int t = t0 + r;
-    u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
-    if (t < C) {
-      const size_t off = ((size_t)t * H + h) * D + c * E;
-      kr = *reinterpret_cast<const u32x4*>(ksrc + off);
-      vr = *reinterpret_cast<const u32x4*>(vsrc + off);
-      float pos[3];
-      wf::rope_token_pos(g, t, fpc, gh, gw, pos);
-      T x[E];
-      __builtin_memcpy(x, &kr, 16);
+    u32x4 kr[HG], vr[HG];
 #pragma unroll
-      for (int k = 0; k < PAIRS; ++k) {
-        float sn, cs;
-        wf::rope_sincos(pos, tab, c * PAIRS + k, sn, cs);
-        wf::rope_rotate_pair(x[2 * k], x[2 * k + 1], cs, sn);
+    for (int i = 0; i < HG; ++i) {
+      kr[i] = u32x4{0u, 0u, 0u, 0u};
+      vr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (t < C && h0 + i < H) {
+        const size_t off = ((size_t)t * H + h0 + i) * D + c * E;
+        kr[i] = *reinterpret_cast<const u32x4*>(ksrc + off);
+        vr[i] = *reinterpret_cast<const u32x4*>(vsrc + off);
       }
-      __builtin_memcpy(&kr, x, 16);
     }
-    *reinterpret_cast<u32x4*>(kt + r * KROW + c * 16) = kr;
-    T vals[E];
-    __builtin_memcpy(vals, &vr, 16);
+    if (t < C) {
+      float pos[3], sn[PAIRS], cs[PAIRS];
+      wf::rope_token_pos(g, t, fpc, gh, gw, pos);
 #pragma unroll
-    for (int e = 0; e < E; ++e) vt[r][c * E + e] = vals[e];
+      for (int k = 0; k < PAIRS; ++k) wf::rope_sincos(pos, tab, c * PAIRS + k, sn[k], cs[k]);
+#pragma unroll
+      for (int i = 0; i < HG; ++i) {
+        T x[E];
+        __builtin_memcpy(x, &kr[i], 16);
+#pragma unroll
+        for (int k = 0; k < PAIRS; ++k) wf::rope_rotate_pair(x[2 * k], x[2 * k + 1], cs[k], sn[k]);
+        __builtin_memcpy(&kr[i], x, 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < HG; ++i) {
+      *reinterpret_cast<u32x4*>(kt[i] + r * KROW + c * 16) = kr[i];
+      T vals[E];
+      __builtin_memcpy(vals, &vr[i], 16);
+#pragma unroll
+      for (int e = 0; e < E; ++e) vt[i][r][c * E + e] = vals[e];
+    }
   }
   __syncthreads();
-  const size_t tile_off = ((size_t)h * (s_pad / 64) + tile) * TILE;
-  {  // K image: piece p, keys key0 .. key0+TG-1 (TG contiguous 16-byte rows)
-    const int p = tid / TG, r = tid % TG;
-    *reinterpret_cast<u32x4*>(kdst + tile_off + p * (64 * 16) + (key0 + r) * 16) =
-        *reinterpret_cast<const u32x4*>(kt + r * KROW + p * 16);
-  }
-  {  // V image: group of E keys (key0/E + grp), dim d
-    const int grp = tid / D, d = tid % D;
-    T vals[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) vals[e] = vt[grp * E + e][d];
-    u32x4 raw;
-    __builtin_memcpy(&raw, vals, 16);
-    *reinterpret_cast<u32x4*>(vdst + tile_off + (key0 / E + grp) * (D * 16) + d * 16) = raw;
+  for (int i = 0; i < HG; ++i) {
+    if (h0 + i >= H) break;
+    const size_t tile_off = ((size_t)(h0 + i) * (s_pad / 64) + tile) * TILE;
+    {  // K image: piece p, keys key0 .. key0+TG-1 (TG contiguous 16-byte rows)
+      const int p = tid / TG, r = tid % TG;
+      *reinterpret_cast<u32x4*>(kdst + tile_off + p * (64 * 16) + (key0 + r) * 16) =
+          *reinterpret_cast<const u32x4*>(kt[i] + r * KROW + p * 16);
+    }
+    {  // V image: group of E keys (key0/E + grp), dim d
+      const int grp = tid / D, d = tid % D;
+      T vals[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) vals[e] = vt[i][grp * E + e][d];
+      u32x4 raw;
+      __builtin_memcpy(&raw, vals, 16);
+      *reinterpret_cast<u32x4*>(vdst + tile_off + (key0 / E + grp) * (D * 16) + d * 16) = raw;
+    }
   }
 }
 
@@ -155,7 +178,8 @@ template <typename T>
 hipError_t launch_rope_tiles(const wf_kv_cache& kv, const void* k, const void* v, char* kdst, char* vdst, int g,
                              hipStream_t s) {
   const int tg = 256 * 16 / (int)sizeof(T) / kv.head_dim;      // tokens per workgroup (as in the kernel)
-  const dim3 grid((kv.chunk_tokens + 63) / 64 * (64 / tg), kv.n_heads);  // slices up to the end of the last tile
+  // slices up to the end of the last tile, by groups of kRopeHeads heads
+  const dim3 grid((kv.chunk_tokens + 63) / 64 * (64 / tg), (kv.n_heads + kRopeHeads - 1) / kRopeHeads);
   const T* kp = static_cast<const T*>(k);
   const T* vp = static_cast<const T*>(v);
   const wf::RopeConfig& rc = kv.rope;

@@ -12,10 +12,10 @@ from workloads import slot_permutation
 
 pytestmark = pytest.mark.gpu
 
-GEOMS = [  # (frames_per_chunk, grid_h, grid_w, head_dim, split)
-    (3, 30, 52, 128, (44, 42, 42)),  # the 832x480 latent grid: 4680 tokens per chunk
-    (3, 4, 5, 128, (44, 42, 42)),    # 60 tokens: ragged against every slice and tile size
-    (2, 3, 7, 64, (22, 22, 20)),     # 42 tokens, head_dim 64
+GEOMS = [  # (frames_per_chunk, grid_h, grid_w, head_dim, split, heads)
+    (3, 30, 52, 128, (44, 42, 42), 12),  # the 832x480 latent grid: 4680 tokens per chunk, 12 heads
+    (3, 4, 5, 128, (44, 42, 42), 3),     # 60 tokens: ragged against every slice and tile size
+    (2, 3, 7, 64, (22, 22, 20), 5),      # 42 tokens, head_dim 64; heads not a multiple of the head group
 ]
 
 
@@ -27,13 +27,13 @@ def _inputs(C, H, D, dt, seed):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("geom", GEOMS, ids=lambda g: f"{g[0]}x{g[1]}x{g[2]}_d{g[3]}")
+@pytest.mark.parametrize("geom", GEOMS, ids=lambda g: f"{g[0]}x{g[1]}x{g[2]}_d{g[3]}_h{g[5]}")
 def test_append_and_refresh_rope_equal_rope_then_write(dtype, geom):
     wf = RL.require_gpu()
-    fpc, gh, gw, D, split = geom
-    C, H = fpc * gh * gw, 3
+    fpc, gh, gw, D, split, H = geom
+    C = fpc * gh * gw
     dt = RL.torch_dtype(dtype)
-    print(f"[case] fused write {dtype} C={C} D={D}", flush=True)
+    print(f"[case] fused write {dtype} C={C} H={H} D={D}", flush=True)
     fused = wf.KVCache(4, C, H, D, dt)
     plain = wf.KVCache(4, C, H, D, dt)
     fused.set_rope(fpc, gh, gw, split)
