@@ -197,6 +197,8 @@ WF_EXPORT int wf_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dt
   if (!aligned(x, 16)) return fail(WF_E_SHAPE, "wf_rope3d: x must be 16-byte aligned");
   if (dtype_size(dtype) == 0) return fail(WF_E_DTYPE, "wf_rope3d: unknown dtype %d", dtype);
   if (n_heads < 1 || n_tokens < 0) return fail(WF_E_SHAPE, "wf_rope3d: non-positive size");
+  // one thread per token and 8-element group: the launch stays below 2^32 work-items
+  if (n_tokens > (1 << 27)) return fail(WF_E_SHAPE, "wf_rope3d: n_tokens %d above 2^27", n_tokens);
   RopeTable t;
   int st = rope_table(head_dim, frames_per_chunk, grid_h, grid_w, d_t, d_h, d_w, theta, t, who);
   if (st != WF_OK) return st;
@@ -277,6 +279,13 @@ static int fill_attn_params(const void* q, const wf_kv_cache* kv, int n_inflight
   if (lse && !aligned(lse, 4)) return fail(WF_E_SHAPE, "%s: lse must be 4-byte aligned", who);
   const long long nq = (long long)n_inflight * kv->chunk_tokens;
   if (nq * kv->n_heads * kv->head_dim >= (1LL << 40)) return fail(WF_E_SHAPE, "%s: query block too large", who);
+  // Work-items per launch must fit in 32 bits: the attention kernels run about two
+  // threads per query row and head, padded to their query tiles, over at most
+  // n_inflight + 1 chunks (the key split adds chunk 0 once more), and the merge one
+  // wave per row and head of a chunk.
+  const long long H = kv->n_heads, C = kv->chunk_tokens;
+  if ((n_inflight + 1LL) * H * (C + 255) * 2 >= (1LL << 32) || C * H * 64 >= (1LL << 32))
+    return fail(WF_E_SHAPE, "%s: %d chunks of %lld tokens x %lld heads exceed one launch", who, n_inflight, C, H);
   std::memset(&p, 0, sizeof p);
   p.q = q;
   p.o = out;

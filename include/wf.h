@@ -141,7 +141,7 @@ int wf_kv_get_table(const wf_kv_cache* kv, int* slots, int cap, int* n);
  *   chunk_tokens = frames_per_chunk * grid_h * grid_w.
  * Angles are fp32 products pos * inv_freq (inv_freq rounded once to fp32);
  * arithmetic is fp32; bf16 results are rounded to nearest even.
- * n_tokens must be a multiple of chunk_tokens.
+ * n_tokens must be a multiple of chunk_tokens and at most 2^27.
  * ------------------------------------------------------------------------ */
 int wf_rope3d(void* x, int n_tokens, int n_heads, int head_dim, int dtype, int first_global_chunk,
               int frames_per_chunk, int grid_h, int grid_w, int d_t, int d_h, int d_w, float theta,
@@ -183,7 +183,9 @@ int wf_kv_refresh_rope(wf_kv_cache* kv, int logical_idx, const void* k, const vo
  * Results are deterministic: bitwise identical run to run, for any physical
  * slot placement, and unaffected by the contents of later chunks.
  * Requires 1 <= n_inflight <= table length, scale > 0, q and out 16-byte
- * aligned.
+ * aligned, and a round that fits one launch:
+ * 2 (n_inflight + 1) n_heads (chunk_tokens + 255) < 2^32 and
+ * 64 chunk_tokens n_heads < 2^32 (WF_E_SHAPE otherwise).
  * ------------------------------------------------------------------------ */
 int wf_chunk_causal_attn_fwd(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
                              void* out, float* lse, void* stream);

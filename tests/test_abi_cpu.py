@@ -190,6 +190,18 @@ def test_attention_argument_errors(L):
     L.wf_kv_cache_destroy(h32)
 
 
+def test_attention_launch_size_limit(L):
+    """A round whose launch would exceed 2^32 work-items is refused on the host:
+    2^20-token chunks x 1024 heads (the largest shape a cache accepts)."""
+    h, pools = make_cache(L, n_slots=2, C=1 << 20, H=1024, D=64)
+    assert set_table(L, h, [0, 1]) == WF_OK
+    q = ctypes.c_void_p(pools.k.value)
+    assert L.wf_chunk_causal_attn_fwd(q, h, 1, 0.1, q, None, None) == WF_E_SHAPE
+    assert b"exceed one launch" in L.wf_last_error()
+    assert L.wf_chunk_causal_attn_fwd_ws(q, h, 1, 0.1, None, q, None, None) == WF_E_SHAPE
+    L.wf_kv_cache_destroy(h)
+
+
 def test_rope_argument_errors(L):
     pools = HostPools()
     x = pools.k
@@ -203,6 +215,7 @@ def test_rope_argument_errors(L):
     assert r(x, 4, 1, 128, 5, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_DTYPE
     assert r(x, 4, 1, 128, 1, -1, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_SHAPE
     assert r(x, 0, 1, 128, 1, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_OK  # nothing to do
+    assert r(x, (1 << 27) + 4, 1, 128, 1, 0, 1, 2, 2, 44, 42, 42, 1e4, None) == WF_E_SHAPE  # launch too large
 
 
 def test_fused_rope_write_argument_errors(L):
