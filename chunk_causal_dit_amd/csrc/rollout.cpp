@@ -89,8 +89,7 @@ WF_EXPORT int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(WF_E_SHAPE, "%s: workspace must be 256-byte aligned", who);
   if (append && kv->free_slots.empty()) return fail(WF_E_FULL, "%s: no free slot for the new chunk", who);
-  if ((long long)N * kv->chunk_tokens * kv->n_heads * kv->head_dim >= (1LL << 40))
-    return fail(WF_E_SHAPE, "%s: query block too large", who);
+  if (const int st = wf::check_attn_size(*kv, N, who); st != WF_OK) return st;
   const bool rope = kv->rope.on;
   const int first = plan->inflight_chunk[0];
   if (rope) {

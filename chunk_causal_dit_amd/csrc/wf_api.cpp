@@ -44,6 +44,18 @@ static int check_shape(int n_slots, int chunk_tokens, int n_heads, int head_dim,
   return ok();
 }
 
+int check_attn_size(const wf_kv_cache& kv, int n_inflight, const char* who) {
+  const long long H = kv.n_heads, C = kv.chunk_tokens;
+  if (n_inflight * C * H * kv.head_dim >= (1LL << 40)) return fail(WF_E_SHAPE, "%s: query block too large", who);
+  // Work-items per launch must fit in 32 bits: the attention kernels run about two
+  // threads per query row and head, padded to their query tiles, over at most
+  // n_inflight + 1 chunks (the key split adds chunk 0 once more), and the merge one
+  // wave per row and head of a chunk.
+  if ((n_inflight + 1LL) * H * (C + 255) * 2 >= (1LL << 32) || C * H * 64 >= (1LL << 32))
+    return fail(WF_E_SHAPE, "%s: %d chunks of %lld tokens x %lld heads exceed one launch", who, n_inflight, C, H);
+  return WF_OK;
+}
+
 }  // namespace wf
 
 using namespace wf;
@@ -277,15 +289,8 @@ static int fill_attn_params(const void* q, const wf_kv_cache* kv, int n_inflight
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(WF_E_SHAPE, "%s: scale must be positive and finite", who);
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(WF_E_SHAPE, "%s: q and out must be 16-byte aligned", who);
   if (lse && !aligned(lse, 4)) return fail(WF_E_SHAPE, "%s: lse must be 4-byte aligned", who);
-  const long long nq = (long long)n_inflight * kv->chunk_tokens;
-  if (nq * kv->n_heads * kv->head_dim >= (1LL << 40)) return fail(WF_E_SHAPE, "%s: query block too large", who);
-  // Work-items per launch must fit in 32 bits: the attention kernels run about two
-  // threads per query row and head, padded to their query tiles, over at most
-  // n_inflight + 1 chunks (the key split adds chunk 0 once more), and the merge one
-  // wave per row and head of a chunk.
-  const long long H = kv->n_heads, C = kv->chunk_tokens;
-  if ((n_inflight + 1LL) * H * (C + 255) * 2 >= (1LL << 32) || C * H * 64 >= (1LL << 32))
-    return fail(WF_E_SHAPE, "%s: %d chunks of %lld tokens x %lld heads exceed one launch", who, n_inflight, C, H);
+  const int st = check_attn_size(*kv, n_inflight, who);
+  if (st != WF_OK) return st;
   std::memset(&p, 0, sizeof p);
   p.q = q;
   p.o = out;

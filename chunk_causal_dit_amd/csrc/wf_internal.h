@@ -51,6 +51,9 @@ inline size_t dtype_size(int dtype) { return dtype == WF_F32 ? 4 : dtype == WF_B
 
 // Records the message in the thread-local error slot and returns code.
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// WF_E_SHAPE (with the message) when an attention round of n_inflight chunks of
+// this cache would not fit one launch; checked before any device work.
+int check_attn_size(const wf_kv_cache& kv, int n_inflight, const char* who);
 
 // ---- kernel launchers (defined in the .hip files); each returns the launch status ----
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

@@ -86,6 +86,19 @@ def test_run_round_refuses_before_enqueuing(L):
     L.wf_kv_cache_destroy(h)
 
 
+def test_run_round_too_large_for_one_launch(L):
+    """A round whose attention launch would exceed 2^32 work-items (2^20-token chunks,
+    1024 heads): WF_E_SHAPE before the append is enqueued, the table unchanged."""
+    h, pools = make_cache(L, n_slots=4, C=1 << 20, H=1024, D=64)
+    a = ctypes.c_void_p(pools.k.value)
+    plan0 = wf.plan_1f1c(4, 6, 2, 0)  # round 0: appends chunk 0, one chunk in flight
+    one = (ctypes.c_void_p * 1)(a.value)
+    assert L.wf_1f1c_run_round(h, ctypes.byref(plan0), a, one, one, 0.1, None, a, None, None) == WF_E_SHAPE
+    assert b"exceed one launch" in L.wf_last_error()
+    assert table(L, h) == []
+    L.wf_kv_cache_destroy(h)
+
+
 def test_run_round_full_cache(L):
     """No free slot for the new chunk: WF_E_FULL before anything is enqueued."""
     h, pools = make_cache(L, n_slots=1, C=64, H=2, D=64)
