@@ -90,6 +90,9 @@ WF_EXPORT int wf_1f1c_run_round(wf_kv_cache* kv, const wf_round_plan* plan, void
     return fail(WF_E_SHAPE, "%s: workspace must be 256-byte aligned", who);
   if (append && kv->free_slots.empty()) return fail(WF_E_FULL, "%s: no free slot for the new chunk", who);
   if (const int st = wf::check_attn_size(*kv, N, who); st != WF_OK) return st;
+  if (const int st = wf::check_workspace_disjoint(*kv, N, workspace, wf::attn_split_bytes(*kv), q, out, lse, who);
+      st != WF_OK)
+    return st;
   const bool rope = kv->rope.on;
   const int first = plan->inflight_chunk[0];
   if (rope) {

@@ -56,6 +56,23 @@ int check_attn_size(const wf_kv_cache& kv, int n_inflight, const char* who) {
   return WF_OK;
 }
 
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_workspace_disjoint(const wf_kv_cache& kv, int n_inflight, const void* ws, size_t ws_bytes, const void* q,
+                             const void* out, const float* lse, const char* who) {
+  const size_t rows = (size_t)n_inflight * kv.chunk_tokens * kv.n_heads;
+  const size_t qb = rows * kv.head_dim * kv.esize, lb = rows * sizeof(float);
+  const size_t pool = (size_t)kv.n_slots * kv.slot_elems * kv.esize;
+  if (overlaps(ws, ws_bytes, q, qb) || overlaps(ws, ws_bytes, out, qb) || overlaps(ws, ws_bytes, lse, lb) ||
+      overlaps(ws, ws_bytes, kv.k_pool, pool) || overlaps(ws, ws_bytes, kv.v_pool, pool))
+    return fail(WF_E_SHAPE, "%s: workspace overlaps q, out, lse or a cache pool", who);
+  return WF_OK;
+}
+
 }  // namespace wf
 
 using namespace wf;
@@ -326,6 +343,8 @@ WF_EXPORT int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, 
   AttnParams p;
   int st = fill_attn_params(q, kv, n_inflight, scale, out, lse, p, who);
   if (st != WF_OK) return st;
+  st = check_workspace_disjoint(*kv, n_inflight, workspace, attn_split_bytes(*kv), q, out, lse, who);
+  if (st != WF_OK) return st;
   return hip_status(launch_attn_fwd(*kv, p, workspace, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -346,6 +365,8 @@ WF_EXPORT int wf_chunk_causal_attn_fwd_i8qk(const void* q, const wf_kv_cache* kv
     return fail(WF_E_SHAPE, "%s: table length x 128-token blocks per chunk exceeds 16384", who);
   AttnParams p;
   int st = fill_attn_params(q, kv, n_inflight, scale, out, lse, p, who);
+  if (st != WF_OK) return st;
+  st = check_workspace_disjoint(*kv, n_inflight, workspace, i8_layout(*kv, n_inflight).total, q, out, lse, who);
   if (st != WF_OK) return st;
   return hip_status(launch_attn_fwd_i8qk(*kv, p, workspace, static_cast<hipStream_t>(stream)), who);
 }

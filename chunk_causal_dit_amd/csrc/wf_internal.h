@@ -54,6 +54,10 @@ int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // WF_E_SHAPE (with the message) when an attention round of n_inflight chunks of
 // this cache would not fit one launch; checked before any device work.
 int check_attn_size(const wf_kv_cache& kv, int n_inflight, const char* who);
+// WF_E_SHAPE when a workspace of ws_bytes (NULL: none) overlaps q, out, lse or a
+// cache pool of an attention round of n_inflight chunks.
+int check_workspace_disjoint(const wf_kv_cache& kv, int n_inflight, const void* ws, size_t ws_bytes, const void* q,
+                             const void* out, const float* lse, const char* who);
 
 // ---- kernel launchers (defined in the .hip files); each returns the launch status ----
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

@@ -206,7 +206,7 @@ int wf_chunk_causal_attn_fwd(const void* q, const wf_kv_cache* kv, int n_infligh
  * 256 bytes f32 [2][H][C][2] their log2-domain row max and weight sum.
  * Calls that share a workspace must be ordered on one stream.
  * Errors: those of wf_chunk_causal_attn_fwd; WF_E_SHAPE for a misaligned
- * workspace. */
+ * workspace or one that overlaps q, out, lse or a cache pool. */
 size_t wf_attn_fwd_workspace_bytes(const wf_kv_cache* kv); /* 0 for fp32 caches */
 
 int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
@@ -225,7 +225,8 @@ int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, int n_infl
  * The mean shift changes no softmax row; lse refers to the unshifted keys
  * (the kernel adds scale * <q^_i, mean_h>, q^ the dequantized query).
  * workspace: device memory of wf_attn_i8qk_workspace_bytes() bytes, 256-byte
- * aligned, caller-owned, overwritten by every call. After a call it holds,
+ * aligned, caller-owned, not overlapping q, out, lse or a cache pool
+ * (WF_E_SHAPE), overwritten by every call. After a call it holds,
  * each array starting at the next multiple of 256 bytes, in this order
  * (n_tab = table length, N = n_inflight, C = chunk_tokens, nb = ceil(C/128)):
  *   f64 [n_tab][H][128]  per-chunk key sums        f32 [H][128] key mean
@@ -315,7 +316,8 @@ int wf_1f1c_plan(int n_steps, int n_chunks, int hist_window, int round, wf_round
  * chunk, [chunk_tokens][n_heads][head_dim] each, 16-byte aligned); run
  * wf_chunk_causal_attn_fwd_ws over the n_inflight chunks (q, out: the round's
  * query block [n_inflight*chunk_tokens][n_heads][head_dim]; lse optional;
- * workspace NULL or of wf_attn_fwd_workspace_bytes(kv) bytes, 256-aligned);
+ * workspace NULL or of wf_attn_fwd_workspace_bytes(kv) bytes, 256-aligned,
+ * disjoint from q, out, lse and the cache pools);
  * evict plan->evict_after oldest entries. The cache table must hold the
  * previous round's state: n_hist + n_inflight entries, less one when a chunk
  * is appended. k and v are host arrays of n_inflight device pointers.

@@ -190,6 +190,35 @@ def test_attention_argument_errors(L):
     L.wf_kv_cache_destroy(h32)
 
 
+def test_workspace_overlap_refused(L):
+    """A workspace that overlaps q, out, lse or a cache pool is refused before any launch."""
+    import torch
+    buf = ctypes.create_string_buffer((1 << 20) + 512)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    q, out = ctypes.c_void_p(base), ctypes.c_void_p(base + (64 << 10))
+    lse_addr = base + (128 << 10)
+    lse = ctypes.cast(ctypes.c_void_p(lse_addr), ctypes.POINTER(ctypes.c_float))
+    fw = L.wf_chunk_causal_attn_fwd_ws
+    h, pools = make_cache(L, n_slots=4)  # bf16, C = 64, H = 2, D = 64
+    assert set_table(L, h, [2, 0, 1]) == WF_OK
+    wsb = L.wf_attn_fwd_workspace_bytes(h)
+    for ws in (q.value, out.value - 256, lse_addr, pools.k.value, pools.v.value + 256):
+        assert fw(q, h, 2, 0.1, ctypes.c_void_p(ws), out, lse, None) == WF_E_SHAPE, hex(ws - base)
+        assert b"overlaps" in L.wf_last_error()
+    if not torch.cuda.is_available():  # disjoint (ending right where q starts): passes the checks, fails at launch
+        ws_end_at_q = ctypes.c_void_p(base + (256 << 10))
+        q2 = ctypes.c_void_p(ws_end_at_q.value + wsb)
+        assert fw(q2, h, 2, 0.1, ws_end_at_q, out, lse, None) == WF_E_HIP
+    L.wf_kv_cache_destroy(h)
+    h, pools = make_cache(L, n_slots=4, D=128)  # the int8 variant
+    assert set_table(L, h, [2, 0, 1]) == WF_OK
+    g = L.wf_chunk_causal_attn_fwd_i8qk
+    assert L.wf_attn_i8qk_workspace_bytes(h, 2) > 0
+    for ws in (q.value, out.value - 256, lse_addr):
+        assert g(q, h, 2, 0.1, ctypes.c_void_p(ws), out, lse, None) == WF_E_SHAPE, hex(ws - base)
+    L.wf_kv_cache_destroy(h)
+
+
 def test_attention_launch_size_limit(L):
     """A round whose launch would exceed 2^32 work-items is refused on the host:
     2^20-token chunks x 1024 heads (the largest shape a cache accepts)."""

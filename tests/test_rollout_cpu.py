@@ -79,6 +79,8 @@ def test_run_round_refuses_before_enqueuing(L):
     assert run(h, ctypes.byref(plan0), ctypes.c_void_p(a.value + 4), one, one, 0.1, None, a, None, None) == WF_E_SHAPE
     wsb = ctypes.c_void_p(a.value + 128)  # workspace not 256-byte aligned
     assert run(h, ctypes.byref(plan0), a, one, one, 0.1, wsb, a, None, None) == WF_E_SHAPE
+    assert run(h, ctypes.byref(plan0), a, one, one, 0.1, a, a, None, None) == WF_E_SHAPE  # workspace overlaps out
+    assert b"overlaps" in L.wf_last_error()
     forged = wf.plan_1f1c(4, 6, 2, 0)
     forged.evict_after = 5
     assert run(h, ctypes.byref(forged), a, one, one, 0.1, None, a, None, None) == WF_E_SHAPE
