@@ -501,6 +501,8 @@ def main():
                     help="run only the W8A8 linear measurement and print its JSON (for profiling)")
     ap.add_argument("--rollout-only", action="store_true",
                     help="run only the 1F1C rollout measurement and print its JSON (for profiling)")
+    ap.add_argument("--i8qk-only", action="store_true",
+                    help="run only the 14B-shaped int8-QK round (--steps timed calls) and print its JSON (for profiling)")
     ap.add_argument("--power-seconds", type=float, default=3.0,
                     help="seconds of back-to-back attention launches with the board power sensor read (0: off)")
     args = ap.parse_args()
@@ -528,6 +530,10 @@ def main():
     split = not args.no_split
     if args.w8a8_only:
         print(json.dumps({"w8a8": bench_w8a8(torch, wf, cfg.nq, args.steps, args.warmup, stream)}), flush=True)
+        return
+    if args.i8qk_only:
+        print(json.dumps({"i8qk": bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], args.steps, args.warmup, stream)}),
+              flush=True)
         return
     if args.rollout_only:
         print(json.dumps({"rollout_1f1c": {

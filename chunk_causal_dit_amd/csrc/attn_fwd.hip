@@ -140,8 +140,8 @@ __device__ __forceinline__ Work decode_block(int b, int N, int H, int T) {
   return w;
 }
 
-// Work item of workgroup b when in-flight chunk 0 is split over its key tiles
-// (split = 2): chunks N-1 .. 1 first, in the order above; then the query tiles of
+// Work item of workgroup b when in-flight chunk 0 is split into two halves of its
+// key tiles (p.split set): chunks N-1 .. 1 first, in the order above; then the query tiles of
 // chunk 0 as 2H "heads" (head h, half p -> 2h + p) in the same XCD-run order, so the
 // short halves fill the end of the grid.
 __device__ __forceinline__ Work decode_work(int b, const wf::AttnParams& p) {
