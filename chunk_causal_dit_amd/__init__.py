@@ -164,6 +164,17 @@ def _dev(t: torch.Tensor, name: str) -> _vp:
     return _vp(t.data_ptr())
 
 
+def _workspace(ws: Optional[torch.Tensor], need: int, where: str) -> Optional[_vp]:
+    """Device pointer of a caller's workspace after checking that it holds need bytes (the
+    C calls take no size: a short buffer would be written past its end)."""
+    if ws is None:
+        return None
+    have = ws.numel() * ws.element_size()
+    if have < need:
+        raise ValueError(f"{where}: workspace holds {have} bytes, the call needs {need}")
+    return _dev(ws, "workspace")
+
+
 def kv_pool_bytes(n_slots: int, chunk_tokens: int, n_heads: int, head_dim: int, dtype: torch.dtype) -> int:
     return int(lib().wf_kv_pool_bytes(n_slots, chunk_tokens, n_heads, head_dim, _DTYPE[dtype]))
 
@@ -325,9 +336,10 @@ def chunk_causal_attn_fwd(q: torch.Tensor, cache: KVCache, n_inflight: int, scal
                                               _dev(out, "out"), lse_p, _vp(_stream(stream))),
                "wf_chunk_causal_attn_fwd")
     else:
-        _check(lib().wf_chunk_causal_attn_fwd_ws(_dev(q, "q"), cache.handle, n_inflight, float(scale),
-                                                 _dev(workspace, "workspace"), _dev(out, "out"), lse_p,
-                                                 _vp(_stream(stream))), "wf_chunk_causal_attn_fwd_ws")
+        ws = _workspace(workspace, attn_fwd_workspace_bytes(cache), "wf_chunk_causal_attn_fwd_ws")
+        _check(lib().wf_chunk_causal_attn_fwd_ws(_dev(q, "q"), cache.handle, n_inflight, float(scale), ws,
+                                                 _dev(out, "out"), lse_p, _vp(_stream(stream))),
+               "wf_chunk_causal_attn_fwd_ws")
     return out, lse
 
 
@@ -340,11 +352,12 @@ def chunk_causal_attn_fwd_i8qk(q: torch.Tensor, cache: KVCache, n_inflight: int,
                                lse: Optional[torch.Tensor] = None, with_lse: bool = True, stream=None):
     """int8-QK variant. Returns (out, lse or None)."""
     out, lse = _attn_io(q, cache, n_inflight, out, lse, with_lse)
+    need = attn_i8qk_workspace_bytes(cache, n_inflight)
     if workspace is None:
-        workspace = torch.empty(max(1, attn_i8qk_workspace_bytes(cache, n_inflight)), dtype=torch.uint8,
-                                device=q.device)
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
     _check(lib().wf_chunk_causal_attn_fwd_i8qk(_dev(q, "q"), cache.handle, n_inflight, float(scale),
-                                               _dev(workspace, "workspace"), _dev(out, "out"),
+                                               _workspace(workspace, need, "wf_chunk_causal_attn_fwd_i8qk"),
+                                               _dev(out, "out"),
                                                _dev(lse, "lse") if lse is not None else None,
                                                _vp(_stream(stream))),
            "wf_chunk_causal_attn_fwd_i8qk")
@@ -422,7 +435,7 @@ def run_round(cache: KVCache, plan: RoundPlan, q: torch.Tensor, ks: Sequence[tor
     kp = (_vp * N)(*[cache._chunk(t, "k").value for t in ks])
     vp = (_vp * N)(*[cache._chunk(t, "v").value for t in vs])
     _check(lib().wf_1f1c_run_round(cache.handle, ctypes.byref(plan), _dev(q, "q"), kp, vp, float(scale),
-                                   _dev(workspace, "workspace") if workspace is not None else None,
+                                   _workspace(workspace, attn_fwd_workspace_bytes(cache), "wf_1f1c_run_round"),
                                    _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
                                    _vp(_stream(stream))), "wf_1f1c_run_round")
     return out, lse

@@ -148,3 +148,24 @@ def test_split_wan13b_4step_sampled_rows():
     RL.assert_close(got, ref_o, "bf16", f"split O chunk 0 ({len(rows)} rows)")
     assert np.abs(lse_s.cpu().numpy()[:, rows] - ref_l).max() <= 2e-3
     assert torch.isfinite(out_s.float()).all()
+
+
+def test_short_workspace_is_refused_before_any_launch():
+    """The binding checks a caller's workspace against the size the call needs (the C
+    calls take no size): one byte short raises, and nothing is enqueued."""
+    wf = RL.require_gpu()
+    C, H, D = 64, 2, 64
+    cache = wf.KVCache(3, C, H, D, torch.bfloat16)
+    kv = torch.zeros(C, H, D, dtype=torch.bfloat16, device="cuda")
+    cache.append(kv, kv)
+    cache.append(kv, kv)
+    q = torch.zeros(2 * C, H, D, dtype=torch.bfloat16, device="cuda")
+    need = wf.attn_fwd_workspace_bytes(cache)
+    short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="workspace holds"):
+        wf.chunk_causal_attn_fwd(q, cache, 2, D ** -0.5, workspace=short)
+    plan = wf.plan_1f1c(1, 3, 1, 1)  # round 1 of a 1-step rollout: chunk 1 appended
+    with pytest.raises(ValueError, match="workspace holds"):
+        wf.run_round(cache, plan, q[:plan.n_inflight * C], [kv] * plan.n_inflight, [kv] * plan.n_inflight,
+                     D ** -0.5, workspace=short)
+    assert cache.table() == [0, 1]
