@@ -372,8 +372,9 @@ def quant_rows_i8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, scales:
     rows, cols = x.shape
     codes = torch.empty((rows, cols), dtype=torch.int8, device=x.device) if codes is None else codes
     scales = torch.empty(rows, dtype=torch.float32, device=x.device) if scales is None else scales
-    if codes.shape != (rows, cols) or codes.dtype != torch.int8 or scales.shape != (rows,):
-        raise ValueError("codes / scales do not match x")
+    if codes.shape != (rows, cols) or codes.dtype != torch.int8 or scales.shape != (rows,) \
+            or scales.dtype != torch.float32:
+        raise ValueError("codes must be int8 [rows][cols] and scales float32 [rows]")
     _check(lib().wf_quant_rows_i8(_dev(x, "x"), rows, cols, WF_BF16, _dev(codes, "codes"), _dev(scales, "scales"),
                                   _vp(_stream(stream))), "wf_quant_rows_i8")
     return codes, scales
@@ -390,6 +391,11 @@ def gemm_w8a8(xq: torch.Tensor, sx: Optional[torch.Tensor], wq: torch.Tensor, sw
     N = wq.shape[0]
     code = {torch.bfloat16: WF_BF16, torch.int32: WF_I32}[out_dtype]
     out = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    if tuple(out.shape) != (M, N) or out.dtype != out_dtype:
+        raise ValueError(f"out must be {out_dtype} [{M}][{N}]")
+    for t, name, n, dt in ((sx, "sx", M, torch.float32), (sw, "sw", N, torch.float32), (bias, "bias", N, torch.bfloat16)):
+        if t is not None and (tuple(t.shape) != (n,) or t.dtype != dt):
+            raise ValueError(f"{name} must be {dt} [{n}]")
     _check(lib().wf_gemm_w8a8(_dev(xq, "xq"), _dev(sx, "sx") if sx is not None else None, _dev(wq, "wq"),
                               _dev(sw, "sw") if sw is not None else None,
                               _dev(bias, "bias") if bias is not None else None, M, N, K, code, _dev(out, "out"),
