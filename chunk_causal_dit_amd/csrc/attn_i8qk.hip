@@ -23,7 +23,6 @@
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int QB = 128;  // quantization block (tokens)
 
@@ -113,8 +112,10 @@ __device__ __forceinline__ void load_mean(const double* partial, int n_tab, int 
 }
 
 // K - mean quantized per 128-token block of one chunk: grid (nb, n_tab, H).
-// The block's keys span two 64-key tile images; 256 threads each take 8
-// 16-byte pieces (key row, 8 dims). Keys past C get code 0.
+// The block's keys span two 64-key tile images; 256 threads each take 4
+// (key row, 16 dims) pieces: two 16-byte bf16 pieces in, one 16-byte piece of
+// codes out, so every load and store instruction of a wave covers 1 KB
+// contiguously. Keys past C get code 0.
 __global__ __launch_bounds__(256) void quant_k_kernel(wf::AttnParams p, const double* partial, float* mean,
                                                       signed char* kcodes, float* kscales, int n_tab) {
   constexpr int D = 128;
@@ -126,54 +127,55 @@ __global__ __launch_bounds__(256) void quant_k_kernel(wf::AttnParams p, const do
   const size_t tile_bytes = 64 * D * 2;
   const char* img = static_cast<const char*>(p.k_pool) + (size_t)p.slots[c] * p.slot_elems * 2 +
                     (size_t)h * p.s_pad * D * 2;
-  // this thread: tile (b*2 + i/1024 ...) positions pos = tid + 256*m, m = 0..7 over 2 tiles x 1024 pieces
-  float xs[8][8];
+  // piece m of this thread: pos = tid + 256 m (m = 0..3) over 2 tiles x 8 code pieces x 64 rows;
+  // code piece q of a row = dims 16q .. 16q+15 = bf16 pieces 2q and 2q+1
+  float xs[4][16];
   float amax = 0.f;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int pos = threadIdx.x + 256 * m;  // 0..2047
-    const int tl = pos >> 10, piece = (pos >> 6) & 15, row = pos & 63;
-    const int t = b * 2 + tl;               // tile inside the chunk
+  for (int m = 0; m < 4; ++m) {
+    const int pos = threadIdx.x + 256 * m;  // 0..1023
+    const int tl = pos >> 9, q = (pos >> 6) & 7, row = pos & 63;
+    const int t = b * 2 + tl;  // tile inside the chunk
     const int key = t * 64 + row;
     const bool ok = key < C && key < (b + 1) * QB;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xs[m][e] = 0.f;
+    for (int e = 0; e < 16; ++e) xs[m][e] = 0.f;
     if (ok) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(img + (size_t)t * tile_bytes + piece * 1024 + row * 16);
-      float x[8];
-      bf16x8_to_f32(raw, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xs[m][e] = x[e] - mean_s[piece * 8 + e];
-        amax = fmaxf(amax, fabsf(xs[m][e]));
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4 raw =
+            *reinterpret_cast<const u32x4*>(img + (size_t)t * tile_bytes + (2 * q + hf) * 1024 + row * 16);
+        float x[8];
+        bf16x8_to_f32(raw, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xs[m][8 * hf + e] = x[e] - mean_s[16 * q + 8 * hf + e];
+          amax = fmaxf(amax, fabsf(xs[m][8 * hf + e]));
+        }
       }
     }
   }
   amax = block_max(amax, red);
   const float s = amax > 0.f ? amax / 127.0f : 1.0f;
   if (threadIdx.x == 0) kscales[((size_t)h * n_tab + c) * nb + b] = s;
-  // int8 image of tile t: [8 pieces of 16 dims][64 rows][16 B]; bf16 piece p -> int8 piece p/2, bytes (p%2)*8
+  // int8 image of tile t: [8 pieces of 16 dims][64 rows][16 B]
   const int tiles = p.s_pad / 64;
   signed char* out = kcodes + (((size_t)c * H + h) * tiles) * (64 * D);
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < 4; ++m) {
     const int pos = threadIdx.x + 256 * m;
-    const int tl = pos >> 10, piece = (pos >> 6) & 15, row = pos & 63;
+    const int tl = pos >> 9, q = (pos >> 6) & 7, row = pos & 63;
     const int t = b * 2 + tl;
     if (t >= tiles) continue;
     const int key = t * 64 + row;
     const bool ok = key < C && key < (b + 1) * QB;
-    unsigned lo = 0, hi = 0;
+    unsigned w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 16; ++e) {
       const unsigned code = ok ? (unsigned)(quant_code(xs[m][e], s) & 0xff) : 0u;
-      if (e < 4)
-        lo |= code << (8 * e);
-      else
-        hi |= code << (8 * (e - 4));
+      w[e >> 2] |= code << (8 * (e & 3));
     }
-    *reinterpret_cast<u32x2*>(out + (size_t)t * (64 * D) + (piece >> 1) * 1024 + row * 16 + (piece & 1) * 8) =
-        u32x2{lo, hi};
+    *reinterpret_cast<u32x4*>(out + (size_t)t * (64 * D) + q * 1024 + row * 16) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
