@@ -308,7 +308,7 @@ def bench_i8qk(torch, wf, cfg, steps, warmup, stream):
     tops = eff / (np.median(ms) / 1e3) / 1e12
     return {
         "workload": f"{cfg.name}: {cfg.description}",
-        "call": "quantize K - mean and Q (3 kernels) + int8-QK attention",
+        "call": "key sums, key mean, quantize K - mean and Q (4 kernels) + int8-QK attention",
         **ms_summary(ms),
         "effective_tops_median": tops,
         "peak_mixed_tops": I8QK_MIXED_PEAK,

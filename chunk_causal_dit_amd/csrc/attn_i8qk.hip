@@ -9,7 +9,7 @@
 // Abstract) without its internals; this is one concrete scheme.
 //
 // Workspace layout (all offsets 256-byte aligned), n_tab = table length:
-//   partial  f64  [n_tab][H][D]        per-chunk key sums
+//   partial  f64  [n_tab][KQ][H][D]    key sums of each quarter of a chunk's key tiles
 //   mean     f32  [H][D]
 //   k_codes  i8   [n_tab][H][tiles][D/16][64][16]   LDS images of 64-key tiles, logical order
 //   k_scales f32  [H][n_tab][nb]       nb = ceil(C / 128)
@@ -25,6 +25,7 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int QB = 128;  // quantization block (tokens)
+constexpr int KQ = 4;    // parts of a chunk's key tiles summed by separate workgroups
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -59,22 +60,24 @@ __device__ __forceinline__ int quant_code(float x, float s) {
   return (int)fminf(fmaxf(c, -127.f), 127.f);
 }
 
-// Per-chunk key sums (float64) for one (table position c, head h): 256 threads
-// = 4 waves; wave w owns 16-byte pieces w, w+4, w+8, w+12 of every tile image
-// (8 dims each), lane r its key row r. Reduction order is fixed.
+// Key sums (float64) of one quarter g of the key tiles of one (table position
+// c, head h): grid (n_tab, H, KQ). 256 threads = 4 waves; wave w owns 16-byte
+// pieces w, w+4, w+8, w+12 of every tile image (8 dims each), lane r its key
+// row r. Reduction order is fixed.
 __global__ __launch_bounds__(256) void k_partial_kernel(wf::AttnParams p, double* partial) {
-  constexpr int D = 128, PIECES = D / 8;
-  const int c = blockIdx.x, h = blockIdx.y, H = p.n_heads, C = p.chunk_tokens;
+  constexpr int D = 128;
+  const int c = blockIdx.x, h = blockIdx.y, g = blockIdx.z, H = p.n_heads, C = p.chunk_tokens;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t tile_bytes = 64 * D * 2;
   const char* img = static_cast<const char*>(p.k_pool) + (size_t)p.slots[c] * p.slot_elems * 2 +
                     (size_t)h * p.s_pad * D * 2;
+  const int t0 = g * p.key_tiles / KQ, t1 = (g + 1) * p.key_tiles / KQ;
   double acc[4][8];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[m][e] = 0.0;
-  for (int t = 0; t < p.key_tiles; ++t) {
+  for (int t = t0; t < t1; ++t) {
     const bool ok = t * 64 + lane < C;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -87,27 +90,29 @@ __global__ __launch_bounds__(256) void k_partial_kernel(wf::AttnParams p, double
         if (ok) acc[m][e] += (double)x[e];
     }
   }
-  double* out = partial + ((size_t)c * H + h) * D;
+  double* out = partial + (((size_t)c * KQ + g) * H + h) * D;
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double s = wave_sum(acc[m][e]);
-      if (lane == 0) out[(wave + 4 * m) * 8 + e] = s;
+      const double sm = wave_sum(acc[m][e]);
+      if (lane == 0) out[(wave + 4 * m) * 8 + e] = sm;
     }
-  (void)PIECES;
 }
 
-// Mean of the visible keys for head h into LDS (fp64 sum in table order, one rounding to fp32).
-__device__ __forceinline__ void load_mean(const double* partial, int n_tab, int H, int h, long long nkv,
-                                          float* mean_s, float* mean_out) {
-  for (int d = threadIdx.x; d < 128; d += blockDim.x) {
-    double s = 0.0;
-    for (int c = 0; c < n_tab; ++c) s += partial[((size_t)c * H + h) * 128 + d];
-    const float m = (float)(s / (double)nkv);
-    mean_s[d] = m;
-    if (mean_out) mean_out[(size_t)h * 128 + d] = m;
-  }
+// Mean of the visible keys: fp64 sum of the key sums in table order, quarter by
+// quarter, one rounding to fp32. Grid H, 128 threads (one per dim).
+__global__ __launch_bounds__(128) void key_mean_kernel(const double* partial, int n_tab, int H, long long nkv,
+                                                       float* mean) {
+  const int h = blockIdx.x, d = threadIdx.x;
+  double s = 0.0;
+  for (int c = 0; c < n_tab; ++c)
+    for (int g = 0; g < KQ; ++g) s += partial[(((size_t)c * KQ + g) * H + h) * 128 + d];
+  mean[(size_t)h * 128 + d] = (float)(s / (double)nkv);
+}
+
+__device__ __forceinline__ void load_mean(const float* mean, int h, float* mean_s) {
+  for (int d = threadIdx.x; d < 128; d += blockDim.x) mean_s[d] = mean[(size_t)h * 128 + d];
   __syncthreads();
 }
 
@@ -116,14 +121,14 @@ __device__ __forceinline__ void load_mean(const double* partial, int n_tab, int 
 // (key row, 16 dims) pieces: two 16-byte bf16 pieces in, one 16-byte piece of
 // codes out, so every load and store instruction of a wave covers 1 KB
 // contiguously. Keys past C get code 0.
-__global__ __launch_bounds__(256) void quant_k_kernel(wf::AttnParams p, const double* partial, float* mean,
-                                                      signed char* kcodes, float* kscales, int n_tab) {
+__global__ __launch_bounds__(256) void quant_k_kernel(wf::AttnParams p, const float* mean, signed char* kcodes,
+                                                      float* kscales, int n_tab) {
   constexpr int D = 128;
   __shared__ float mean_s[D];
   __shared__ float red[4];
   const int b = blockIdx.x, c = blockIdx.y, h = blockIdx.z, H = p.n_heads, C = p.chunk_tokens;
   const int nb = (C + QB - 1) / QB;
-  load_mean(partial, n_tab, H, h, (long long)n_tab * C, mean_s, (b == 0 && c == 0) ? mean : nullptr);
+  load_mean(mean, h, mean_s);
   const size_t tile_bytes = 64 * D * 2;
   const char* img = static_cast<const char*>(p.k_pool) + (size_t)p.slots[c] * p.slot_elems * 2 +
                     (size_t)h * p.s_pad * D * 2;
@@ -181,14 +186,14 @@ __global__ __launch_bounds__(256) void quant_k_kernel(wf::AttnParams p, const do
 
 // Q quantized per 128-token block of one in-flight chunk: grid (nb, N, H).
 // Thread i takes query row i/2 of the block and half (i%2) of head_dim.
-__global__ __launch_bounds__(256) void quant_q_kernel(wf::AttnParams p, const double* partial, signed char* qcodes,
-                                                      float* qscales, float* qm, int n_tab) {
+__global__ __launch_bounds__(256) void quant_q_kernel(wf::AttnParams p, const float* mean, signed char* qcodes,
+                                                      float* qscales, float* qm) {
   constexpr int D = 128;
   __shared__ float mean_s[D];
   __shared__ float red[4];
   const int b = blockIdx.x, j = blockIdx.y, h = blockIdx.z, H = p.n_heads, C = p.chunk_tokens;
   const int nb = (C + QB - 1) / QB;
-  load_mean(partial, n_tab, H, h, (long long)n_tab * C, mean_s, nullptr);
+  load_mean(mean, h, mean_s);
   const int r = b * QB + (threadIdx.x >> 1), half = threadIdx.x & 1;
   const bool ok = r < C;
   const size_t row = (size_t)j * C + r;
@@ -242,7 +247,7 @@ I8Layout i8_layout(const wf_kv_cache& kv, int n_inflight) {
   L.blocks_per_chunk = (int)((C + QB - 1) / QB);
   size_t off = 0;
   L.partial = off;
-  off = align256(off + (size_t)n_tab * H * D * sizeof(double));
+  off = align256(off + (size_t)n_tab * KQ * H * D * sizeof(double));
   L.mean = off;
   off = align256(off + H * D * sizeof(float));
   L.k_codes = off;
@@ -271,17 +276,20 @@ hipError_t launch_quant_i8(const wf_kv_cache& kv, AttnParams& p, void* workspace
   p.k_scales = reinterpret_cast<const float*>(ws + L.k_scales);
   p.qm = reinterpret_cast<const float*>(ws + L.qm);
   double* partial = reinterpret_cast<double*>(ws + L.partial);
-  k_partial_kernel<<<dim3(n_tab, kv.n_heads), 256, 0, s>>>(p, partial);
+  k_partial_kernel<<<dim3(n_tab, kv.n_heads, KQ), 256, 0, s>>>(p, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  float* mean = reinterpret_cast<float*>(ws + L.mean);
+  key_mean_kernel<<<kv.n_heads, 128, 0, s>>>(partial, n_tab, kv.n_heads, (long long)n_tab * kv.chunk_tokens, mean);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   quant_k_kernel<<<dim3(L.blocks_per_chunk, n_tab, kv.n_heads), 256, 0, s>>>(
-      p, partial, reinterpret_cast<float*>(ws + L.mean), reinterpret_cast<signed char*>(ws + L.k_codes),
-      reinterpret_cast<float*>(ws + L.k_scales), n_tab);
+      p, mean, reinterpret_cast<signed char*>(ws + L.k_codes), reinterpret_cast<float*>(ws + L.k_scales), n_tab);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   quant_q_kernel<<<dim3(L.blocks_per_chunk, p.n_inflight, kv.n_heads), 256, 0, s>>>(
-      p, partial, reinterpret_cast<signed char*>(ws + L.q_codes), reinterpret_cast<float*>(ws + L.q_scales),
-      reinterpret_cast<float*>(ws + L.qm), n_tab);
+      p, mean, reinterpret_cast<signed char*>(ws + L.q_codes), reinterpret_cast<float*>(ws + L.q_scales),
+      reinterpret_cast<float*>(ws + L.qm));
   return hipGetLastError();
 }
 

@@ -229,7 +229,8 @@ int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, int n_infl
  * (WF_E_SHAPE), overwritten by every call. After a call it holds,
  * each array starting at the next multiple of 256 bytes, in this order
  * (n_tab = table length, N = n_inflight, C = chunk_tokens, nb = ceil(C/128)):
- *   f64 [n_tab][H][128]  per-chunk key sums        f32 [H][128] key mean
+ *   f64 [n_tab][4][H][128]  key sums of each quarter of a chunk's 64-key tiles
+ *       (tiles [g*T/4, (g+1)*T/4), T = ceil(C/64))   f32 [H][128] key mean
  *   i8  [n_tab][H][S_pad/64][8][64][16]  K - mean codes as 64-key tile images
  *       (16-dim pieces, key-major), in table order, zero past each chunk end
  *   f32 [H][n_tab][nb] K block scales   i8 [N*C][H][128] Q codes

@@ -28,7 +28,7 @@ def workspace_layout(n_tab, H, D, C, s_pad, N):
     a = lambda x: (x + 255) // 256 * 256
     nb = -(-C // 128)
     L, off = {}, 0
-    for name, size in (("partial", n_tab * H * D * 8), ("mean", H * D * 4), ("k_codes", n_tab * H * s_pad * D),
+    for name, size in (("partial", n_tab * 4 * H * D * 8), ("mean", H * D * 4), ("k_codes", n_tab * H * s_pad * D),
                        ("k_scales", n_tab * H * nb * 4), ("q_codes", N * C * H * D),
                        ("q_scales", H * N * nb * 4), ("qm", H * N * C * 4)):
         L[name] = (off, size)
