@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void k_partial_kernel(wf::AttnParams p, double
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[m][e] = 0.0;
-  for (int t = t0; t < t1; ++t) {
+#pragma unroll 4
+  for (int t = t0; t < t1; ++t) {  // unrolled: the loads of four tiles in flight, adds in tile order
     const bool ok = t * 64 + lane < C;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
