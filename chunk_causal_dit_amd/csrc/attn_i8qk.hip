@@ -1,6 +1,8 @@
 // int8-QK variant of the round's attention: quantization of K and Q into the
 // caller's workspace. The scheme (include/wf.h): one per-(head, channel) key
-// mean over all keys the round can see (float64 sum, rounded once to fp32);
+// mean over the keys every query chunk sees, the history chunks and in-flight
+// chunk 0 (float64 sum, rounded once to fp32), so that no chunk's codes depend
+// on a later chunk (chunk-wise causal attention, Abstract);
 // Q and K - mean cut per head into 128-token blocks that start at every chunk
 // start; per block s = amax / 127 (1 when amax = 0) and code =
 // clamp(round_half_even(x / s), -127, 127), every decision in fp32 with a
@@ -8,8 +10,9 @@
 // (SageAttention) for their DiT-only tests (Wave Forcing paper pages,
 // Abstract) without its internals; this is one concrete scheme.
 //
-// Workspace layout (all offsets 256-byte aligned), n_tab = table length:
-//   partial  f64  [n_tab][KQ][H][D]    key sums of each quarter of a chunk's key tiles
+// Workspace layout (all offsets 256-byte aligned), n_tab = table length,
+// n_mean = n_hist + 1 (the chunks the key mean is taken over):
+//   partial  f64  [n_mean][KQ][H][D]   key sums of each quarter of a chunk's key tiles
 //   mean     f32  [H][D]
 //   k_codes  i8   [n_tab][H][tiles][D/16][64][16]   LDS images of 64-key tiles, logical order
 //   k_scales f32  [H][n_tab][nb]       nb = ceil(C / 128)
@@ -61,9 +64,9 @@ __device__ __forceinline__ int quant_code(float x, float s) {
 }
 
 // Key sums (float64) of one quarter g of the key tiles of one (table position
-// c, head h): grid (n_tab, H, KQ). 256 threads = 4 waves; wave w owns 16-byte
-// pieces w, w+4, w+8, w+12 of every tile image (8 dims each), lane r its key
-// row r. Reduction order is fixed.
+// c, head h): grid (n_mean, H, KQ), c < n_mean = n_hist + 1. 256 threads = 4
+// waves; wave w owns 16-byte pieces w, w+4, w+8, w+12 of every tile image (8
+// dims each), lane r its key row r. Reduction order is fixed.
 __global__ __launch_bounds__(256) void k_partial_kernel(wf::AttnParams p, double* partial) {
   constexpr int D = 128;
   const int c = blockIdx.x, h = blockIdx.y, g = blockIdx.z, H = p.n_heads, C = p.chunk_tokens;
@@ -101,15 +104,16 @@ __global__ __launch_bounds__(256) void k_partial_kernel(wf::AttnParams p, double
     }
 }
 
-// Mean of the visible keys: fp64 sum of the key sums in table order, quarter by
-// quarter, one rounding to fp32. Grid H, 128 threads (one per dim).
-__global__ __launch_bounds__(128) void key_mean_kernel(const double* partial, int n_tab, int H, long long nkv,
+// Mean of the keys of the first n_mean table entries: fp64 sum of the key sums
+// in table order, quarter by quarter, one rounding to fp32. Grid H, 128
+// threads (one per dim).
+__global__ __launch_bounds__(128) void key_mean_kernel(const double* partial, int n_mean, int H, long long nkeys,
                                                        float* mean) {
   const int h = blockIdx.x, d = threadIdx.x;
   double s = 0.0;
-  for (int c = 0; c < n_tab; ++c)
+  for (int c = 0; c < n_mean; ++c)
     for (int g = 0; g < KQ; ++g) s += partial[(((size_t)c * KQ + g) * H + h) * 128 + d];
-  mean[(size_t)h * 128 + d] = (float)(s / (double)nkv);
+  mean[(size_t)h * 128 + d] = (float)(s / (double)nkeys);
 }
 
 __device__ __forceinline__ void load_mean(const float* mean, int h, float* mean_s) {
@@ -247,8 +251,9 @@ I8Layout i8_layout(const wf_kv_cache& kv, int n_inflight) {
   const size_t H = kv.n_heads, D = kv.head_dim, C = kv.chunk_tokens;
   L.blocks_per_chunk = (int)((C + QB - 1) / QB);
   size_t off = 0;
+  const int n_mean = n_tab - n_inflight + 1;  // history + in-flight chunk 0
   L.partial = off;
-  off = align256(off + (size_t)n_tab * KQ * H * D * sizeof(double));
+  off = align256(off + (size_t)n_mean * KQ * H * D * sizeof(double));
   L.mean = off;
   off = align256(off + H * D * sizeof(float));
   L.k_codes = off;
@@ -277,11 +282,13 @@ hipError_t launch_quant_i8(const wf_kv_cache& kv, AttnParams& p, void* workspace
   p.k_scales = reinterpret_cast<const float*>(ws + L.k_scales);
   p.qm = reinterpret_cast<const float*>(ws + L.qm);
   double* partial = reinterpret_cast<double*>(ws + L.partial);
-  k_partial_kernel<<<dim3(n_tab, kv.n_heads, KQ), 256, 0, s>>>(p, partial);
+  const int n_mean = p.n_hist + 1;  // the key mean covers history + in-flight chunk 0
+  k_partial_kernel<<<dim3(n_mean, kv.n_heads, KQ), 256, 0, s>>>(p, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   float* mean = reinterpret_cast<float*>(ws + L.mean);
-  key_mean_kernel<<<kv.n_heads, 128, 0, s>>>(partial, n_tab, kv.n_heads, (long long)n_tab * kv.chunk_tokens, mean);
+  key_mean_kernel<<<kv.n_heads, 128, 0, s>>>(partial, n_mean, kv.n_heads, (long long)n_mean * kv.chunk_tokens,
+                                             mean);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   quant_k_kernel<<<dim3(L.blocks_per_chunk, n_tab, kv.n_heads), 256, 0, s>>>(

@@ -216,7 +216,11 @@ int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, int n_infl
  * int8-QK variant (bf16 caches, head_dim 128). The pages name a
  * quantized-QK attention backend (SageAttention) in their DiT-only tests
  * (Abstract) without its internals; this call implements one scheme:
- *   mean_h = per-(head, channel) mean of all visible keys (fp64 sum, fp32);
+ *   mean_h = per-(head, channel) mean of the keys every query chunk sees:
+ *   the n_hist history chunks and in-flight chunk 0 (fp64 sum, rounded once
+ *   to fp32). No later in-flight chunk enters it, so chunk j's output depends
+ *   on chunks 0..n_hist+j only (chunk-wise causal attention, Abstract; K/V
+ *   handed one way from earlier to later chunks, airadar.tv summaries);
  *   Q and K - mean are quantized per head in blocks of 128 tokens that start
  *   at every chunk start: s = amax/127 (1 if amax = 0), code =
  *   clamp(round_half_even(x/s), -127, 127), all decisions in fp32;
@@ -229,7 +233,8 @@ int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, int n_infl
  * (WF_E_SHAPE), overwritten by every call. After a call it holds,
  * each array starting at the next multiple of 256 bytes, in this order
  * (n_tab = table length, N = n_inflight, C = chunk_tokens, nb = ceil(C/128)):
- *   f64 [n_tab][4][H][128]  key sums of each quarter of a chunk's 64-key tiles
+ *   f64 [n_hist+1][4][H][128]  key sums of each quarter of the 64-key tiles
+ *       of history chunk c (c < n_hist) or in-flight chunk 0 (c = n_hist)
  *       (tiles [g*T/4, (g+1)*T/4), T = ceil(C/64))   f32 [H][128] key mean
  *   i8  [n_tab][H][S_pad/64][8][64][16]  K - mean codes as 64-key tile images
  *       (16-dim pieces, key-major), in table order, zero past each chunk end

@@ -37,7 +37,6 @@ __all__ = [
     "chunk_causal_attention",
     "dense_masked_attention",
     "bruteforce_attention",
-    "softmax_weights",
 ]
 
 
@@ -180,12 +179,3 @@ def bruteforce_attention(q, k_vis, v_vis, n_hist, chunk_tokens, scale):
                 out[i, h, d] = acc / tot
             lse[h, i] = m + math.log(tot)
     return out, lse
-
-
-def softmax_weights(q, k_vis, n_hist, chunk_tokens, scale, h, i):
-    """Attention weights of query row i, head h, over its visible keys (float64)."""
-    C = chunk_tokens
-    L = visible_key_count(i // C, n_hist, C)
-    s = (k_vis[:L, h, :].astype(np.float64) @ q[i, h, :].astype(np.float64)) * scale
-    p = np.exp(s - s.max())
-    return p / p.sum()

@@ -6,9 +6,14 @@ none of its internals. The scheme here is the one the 14B-shaped workload
 fixes, with these readings where it is open:
   * per head, Q and K are cut into blocks of 128 tokens that start at every
     chunk start (the last block of a 4680-token chunk holds 72 tokens);
-  * K is first shifted by one per-(head, channel) mean taken over all keys the
-    round can see; one shift for every key keeps each query's softmax exact,
-    because it adds the same constant <q_i, mean> to all of row i's logits;
+  * K is first shifted by one per-(head, channel) mean taken over the keys that
+    every query chunk of the round sees: the history chunks and in-flight
+    chunk 0 (the refresh chunk). One shift for every key keeps each query's
+    softmax exact, because it adds the same constant <q_i, mean> to all of row
+    i's logits; taking it over that common prefix keeps the round chunk-wise
+    causal, since no later in-flight chunk's keys enter it (Abstract: a chunk
+    reads only earlier chunks; airadar.tv summaries, first paragraph: K/V pass
+    one way, from earlier chunks to later ones);
   * per block: a = max |x|, scale s = a / 127 (s = 1 when a = 0), code
     q = clip(round_half_even(x / s), -127, 127);
   * every decision that yields an integer (the shifted value, the scale, the
@@ -32,9 +37,14 @@ __all__ = ["BLOCK", "key_channel_mean", "quantize_chunk_blocks", "dequantize",
 BLOCK = 128
 
 
-def key_channel_mean(k_vis: np.ndarray) -> np.ndarray:
-    """Per-(head, channel) mean over all visible keys: [H][D] float32 (fp64 sum)."""
-    return (k_vis.astype(np.float64).sum(axis=0) / k_vis.shape[0]).astype(np.float32)
+def key_channel_mean(k_vis: np.ndarray, n_hist: int, chunk_tokens: int) -> np.ndarray:
+    """Per-(head, channel) mean of the keys every query chunk sees, i.e. the
+    first (n_hist + 1) * C keys of the logical order (history, then in-flight
+    chunk 0): [H][D] float32, summed in float64 and rounded once."""
+    L = (n_hist + 1) * chunk_tokens
+    if k_vis.shape[0] < L:
+        raise ValueError("fewer keys than history plus the refresh chunk")
+    return (np.asarray(k_vis[:L], dtype=np.float64).sum(axis=0) / L).astype(np.float32)
 
 
 def quantize_chunk_blocks(x: np.ndarray, chunk_tokens: int, block: int = BLOCK
@@ -75,9 +85,9 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, chunk_tokens: int,
     return codes.astype(np.float64) * s[:, :, None]
 
 
-def quantize_round(q: np.ndarray, k_vis: np.ndarray, chunk_tokens: int):
+def quantize_round(q: np.ndarray, k_vis: np.ndarray, n_hist: int, chunk_tokens: int):
     """Quantize one round: returns dict with mean [H][D] f32, K' codes/scales, Q codes/scales."""
-    mean = key_channel_mean(k_vis)
+    mean = key_channel_mean(k_vis, n_hist, chunk_tokens)
     k_shift = (np.asarray(k_vis, np.float32) - mean[None, :, :]).astype(np.float32)
     kq, ks = quantize_chunk_blocks(k_shift, chunk_tokens)
     qq, qs = quantize_chunk_blocks(q, chunk_tokens)
@@ -89,7 +99,7 @@ def quantized_attention(q, k_vis, v_vis, n_hist, chunk_tokens, scale, rows=None,
                         workers=1, quant=None):
     """Exact attention on the dequantized operands (the int8 path's target)."""
     if quant is None:
-        quant = quantize_round(q, k_vis, chunk_tokens)
+        quant = quantize_round(q, k_vis, n_hist, chunk_tokens)
     q_hat = dequantize(quant["q_codes"], quant["q_scales"], chunk_tokens)
     k_hat = dequantize(quant["k_codes"], quant["k_scales"], chunk_tokens)
     k_hat = k_hat + quant["mean"].astype(np.float64)[None, :, :]

@@ -18,6 +18,10 @@ import oracle.attention as OA  # noqa: E402
 
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_REL = 5e-3
+# per (query row, head): sum_d |o - ref| / sum_d |ref| over head_dim. Measured at most
+# 3.4e-3 on every full-size round (p50 2.3e-3, from bf16 weights and the bf16 output);
+# one dropped or doubled 64-key tile moves a row of a 32,760-key round by about 4 %.
+BF16_ROW_REL = 6e-3
 F32_MAX_ABS = 1e-4
 
 
@@ -109,15 +113,33 @@ def error_stats(gpu: np.ndarray, ref: np.ndarray):
     return float(d.max()), float(d.sum() / np.abs(ref).sum())
 
 
+def row_rel_errors(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per (row, head) relative error over the last axis: sum |o - ref| / sum |ref|."""
+    d = np.abs(gpu.astype(np.float64) - ref).sum(axis=-1)
+    return d / np.maximum(np.abs(ref).sum(axis=-1), 1e-300)
+
+
 def assert_close(gpu_out, ref_out, dtype: str, what: str = "O"):
+    """Aggregate bounds (max abs, mean relative error over all outputs) and, for
+    bf16, the per-row bound BF16_ROW_REL on every (row, head) of a [rows][H][D]
+    output, so that one wrong row cannot hide in the aggregate."""
     mx, rel = error_stats(gpu_out, ref_out)
-    print(f"[parity] {what}: max abs {mx:.3e}, mean rel {rel:.3e}", flush=True)
+    msg = f"[parity] {what}: max abs {mx:.3e}, mean rel {rel:.3e}"
+    rows = None
+    if dtype != "f32" and np.ndim(ref_out) == 3:
+        rows = row_rel_errors(gpu_out, ref_out)
+        msg += (f", per-row rel p50 {np.median(rows):.2e} p99.9 {np.quantile(rows, 0.999):.2e} "
+                f"max {rows.max():.2e} over {rows.size} rows")
+    print(msg, flush=True)
     assert np.isfinite(gpu_out).all(), f"{what}: non-finite values"
     if dtype == "f32":
         assert mx <= F32_MAX_ABS, f"{what}: max abs {mx} > {F32_MAX_ABS}"
     else:
         assert mx <= BF16_MAX_ABS, f"{what}: max abs {mx} > {BF16_MAX_ABS}"
         assert rel <= BF16_MEAN_REL, f"{what}: mean rel {rel} > {BF16_MEAN_REL}"
+        if rows is not None:
+            worst = np.unravel_index(np.argmax(rows), rows.shape)
+            assert rows.max() <= BF16_ROW_REL, f"{what}: row {worst} rel {rows.max()} > {BF16_ROW_REL}"
     return mx, rel
 
 

@@ -112,9 +112,8 @@ def test_step5_round_refresh_overwrites_stale_slot():
     outs = {"whole": wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale),
             "split": wf.chunk_causal_attn_fwd(q, cache, N, cfg.scale, workspace=RL.split_workspace(wf, cache))}
     torch.cuda.synchronize()
-    rows = RL.boundary_rows(C, N, 8, seed=3)
-    ref_o, ref_l = RL.oracle_round(inp, rows=rows)
+    ref_o, ref_l = RL.oracle_round(inp)  # every row of the round
     for name, (out, lse) in outs.items():
-        got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
-        RL.assert_close(got, ref_o, "bf16", f"O ({len(rows)} rows, {name})")
-        assert np.abs(lse.cpu().numpy()[:, rows] - ref_l).max() <= 2e-3, name
+        got = out.float().cpu().numpy()
+        RL.assert_close(got, ref_o, "bf16", f"O (all {got.shape[0]} rows, {name})")
+        assert np.abs(lse.cpu().numpy() - ref_l).max() <= 2e-3, name

@@ -27,8 +27,9 @@ def workspace_layout(n_tab, H, D, C, s_pad, N):
     """Byte offsets of the workspace arrays, in the order and alignment include/wf.h documents."""
     a = lambda x: (x + 255) // 256 * 256
     nb = -(-C // 128)
+    n_mean = n_tab - N + 1  # the key mean covers the history and in-flight chunk 0
     L, off = {}, 0
-    for name, size in (("partial", n_tab * 4 * H * D * 8), ("mean", H * D * 4), ("k_codes", n_tab * H * s_pad * D),
+    for name, size in (("partial", n_mean * 4 * H * D * 8), ("mean", H * D * 4), ("k_codes", n_tab * H * s_pad * D),
                        ("k_scales", n_tab * H * nb * 4), ("q_codes", N * C * H * D),
                        ("q_scales", H * N * nb * 4), ("qm", H * N * C * 4)):
         L[name] = (off, size)
@@ -80,7 +81,7 @@ def visible_keys(inp):
 def check_quantization(inp, cache, ws):
     cfg = inp.cfg
     k_vis, _ = visible_keys(inp)
-    ref = OQ.quantize_round(inp.q, k_vis, cfg.chunk_tokens)
+    ref = OQ.quantize_round(inp.q, k_vis, cfg.n_hist, cfg.chunk_tokens)
     got = read_workspace(ws, cache, cfg.n_inflight)
     assert got["total"] == ws.numel(), "workspace layout differs from the documented one"
     assert np.array_equal(got["mean"], ref["mean"]), "key mean"
@@ -113,7 +114,8 @@ def check_outputs(inp, out, lse, ref_quant, rows=None):
     print(f"[parity] {cfg.name} LSE vs quantized oracle: max abs {dl:.3e}", flush=True)
     assert dl <= LSE_ATOL
     mx, rel = RL.error_stats(got, o_x)
-    cos = float((got.astype(np.float64) * o_x).sum() / np.linalg.norm(got) / np.linalg.norm(o_x))
+    g64 = got.astype(np.float64)
+    cos = float((g64 * o_x).sum() / np.linalg.norm(g64) / np.linalg.norm(o_x))
     print(f"[parity] {cfg.name} O vs exact oracle: max abs {mx:.3e}, mean rel {rel:.3e}, cosine {cos:.6f}",
           flush=True)
     assert rel <= I8_MEAN_REL_EXACT and cos >= I8_COSINE
@@ -138,17 +140,17 @@ def test_i8_small_full_parity(cfg):
     check_outputs(inp, out, lse, ref)
 
 
-def test_i8_14b_round_sampled():
+def test_i8_14b_round_all_rows():
     """The 14B-shaped round (40 heads, 4680-token chunks, 5 in flight, 2 history):
-    quantization bit-exact in full, attention on sampled rows."""
+    quantization bit-exact in full, attention on every one of its 23,400 query rows
+    and 40 heads."""
     wf = RL.require_gpu()
     cfg = CONFIGS["i8qk_14b"]
     print(f"[case] {cfg.name}", flush=True)
     inp = make_round_inputs(cfg)
     out, lse, cache, ws = run_i8(wf, inp)
     ref = check_quantization(inp, cache, ws)
-    rows = RL.boundary_rows(cfg.chunk_tokens, cfg.n_inflight, 6, seed=9)
-    check_outputs(inp, out, lse, ref, rows=rows)
+    check_outputs(inp, out, lse, ref)
 
 
 def test_i8_permuted_slots_bitwise():
@@ -188,20 +190,28 @@ def test_i8_constant_keys_average_values():
         np.testing.assert_allclose(lse.cpu().numpy()[:, j * C:(j + 1) * C], want, atol=1e-3, rtol=0)
 
 
-def test_i8_later_chunks_do_not_change_earlier_outputs():
-    """Perturbing the last in-flight chunk changes the shared key mean and so
-    the codes of every chunk; but with K of the last chunk unchanged (Q and V
-    perturbed), earlier chunks' outputs stay bitwise equal."""
+@pytest.mark.parametrize("j", [0, 1, 2])
+def test_i8_later_chunks_do_not_change_earlier_outputs(j):
+    """Q, K and V of every in-flight chunk after chunk j perturbed: the key mean
+    covers only history and in-flight chunk 0, so chunks 0..j keep bitwise equal
+    codes, O and LSE, while the perturbed chunks' outputs change."""
     wf = RL.require_gpu()
     cfg = RoundConfig("i8_caus", 2, 128, 300, 4, 2, "bf16", seed=58, int8_qk=True)
     inp = make_round_inputs(cfg)
-    o0, l0, _, _ = run_i8(wf, inp)
+    o0, l0, c0, w0 = run_i8(wf, inp)
+    g0 = read_workspace(w0, c0, cfg.n_inflight)
     C = cfg.chunk_tokens
-    lo = (cfg.n_inflight - 1) * C
-    rng = np.random.default_rng(7)
-    inp.q[lo:] = round_to_bf16(rng.standard_normal(inp.q[lo:].shape).astype(np.float32) * 3)
-    inp.v_in[lo:] = round_to_bf16(rng.standard_normal(inp.v_in[lo:].shape).astype(np.float32) * 3)
-    o1, l1, _, _ = run_i8(wf, inp)
+    lo = (j + 1) * C
+    rng = np.random.default_rng(7 + j)
+    draw = lambda a: round_to_bf16(rng.standard_normal(a.shape).astype(np.float32) * 3)
+    inp.q[lo:] = draw(inp.q[lo:])
+    inp.k_in[lo:] = draw(inp.k_in[lo:])
+    inp.v_in[lo:] = draw(inp.v_in[lo:])
+    o1, l1, c1, w1 = run_i8(wf, inp)
+    g1 = read_workspace(w1, c1, cfg.n_inflight)
+    assert np.array_equal(g1["mean"], g0["mean"])
+    nk = (cfg.n_hist + j + 1) * C
+    assert np.array_equal(g1["k_codes"][:nk], g0["k_codes"][:nk])
     assert torch.equal(o1[:lo], o0[:lo]) and torch.equal(l1[:, :lo], l0[:, :lo])
     assert not torch.equal(o1[lo:], o0[lo:])
 

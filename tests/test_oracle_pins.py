@@ -170,13 +170,23 @@ def test_q_zero_closed_form():
 
 
 def test_softmax_rows_sum_to_one():
-    q, k, _ = _round_inputs(5, 3, 2, 2, 8, 71)
-    for h in range(2):
-        for i in range(15):
-            w = A.softmax_weights(q, k, 2, 5, 0.4, h, i)
-            assert len(w) == (2 + i // 5 + 1) * 5
-            assert abs(w.sum() - 1.0) <= 1e-15
-            assert (w > 0).all()
+    """With V the identity over keys (value of key k = unit vector e_k), a row of O
+    is that row's softmax weights: they sum to 1, vanish exactly on invisible keys,
+    and two visible keys' weights stand in the ratio exp(scale * score difference)."""
+    C, N, Hs, H, scale = 5, 3, 2, 2, 0.4
+    nk = (Hs + N) * C
+    q, k, _ = _round_inputs(C, N, Hs, H, nk, 71)  # head_dim = key count, so V can be the identity
+    v = np.broadcast_to(np.eye(nk)[:, None, :], (nk, H, nk)).copy()
+    o, _ = ATTN(q, k, v, Hs, C, scale)
+    for h in range(H):
+        for i in range(N * C):
+            w = o[i, h]
+            L = (Hs + i // C + 1) * C
+            assert abs(w.sum() - 1.0) <= 1e-14
+            assert (w[:L] > 0).all() and not w[L:].any()
+            a, b = 0, L - 1
+            want = math.exp(scale * float(np.dot(q[i, h], k[a, h] - k[b, h])))
+            assert abs(w[a] / w[b] / want - 1.0) <= 1e-12
 
 
 def test_single_visible_key_returns_its_value():
@@ -302,6 +312,120 @@ def test_int8_kmean_shift_keeps_attention_exact():
     o2, l2 = ATTN(q, k - mean[None], v, Hs, C, 0.35)
     np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
     np.testing.assert_allclose(l2 + 0.35 * np.einsum("ihd,hd->hi", q, mean), l1, atol=1e-12)
+
+
+def _kmean_golden():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "int8_kmean_hand_example.txt"))
+            if l.strip() and not l.startswith("#")]
+    g = {"key": [], "block": []}
+    for r in rows:
+        if r[0] in ("key", "block"):
+            g[r[0]].append([float(x) for x in r[1:]])
+        else:
+            g[r[0]] = [float(x) for x in r[1:]]
+    return g
+
+
+def check_kmean_golden(quantize_round):
+    """The hand-derived key mean, K' block scales and codes (tests/golden)."""
+    g = _kmean_golden()
+    C, Hs = int(g["chunk_tokens"][0]), int(g["n_hist"][0])
+    k = np.array(g["key"], dtype=np.float32)[:, None, :]  # [8][1 head][2 channels]
+    n_chunks = k.shape[0] // C
+    q = np.zeros(((n_chunks - Hs) * C, 1, 2), dtype=np.float32)
+    r = quantize_round(q, k, Hs, C)
+    np.testing.assert_array_equal(r["mean"], np.array([g["mean"]], dtype=np.float32))
+    for c, blk in enumerate(g["block"]):
+        assert r["k_scales"][0, c] == np.float32(blk[0]) / np.float32(127), f"chunk {c} scale"
+        np.testing.assert_array_equal(r["k_codes"][c * C:(c + 1) * C, 0, :].ravel().astype(np.int64),
+                                      np.array(blk[1:], dtype=np.int64), err_msg=f"chunk {c} codes")
+
+
+def check_quantized_causality(quantize_round):
+    """Quantized attention is chunk-wise causal too: Q, K and V of the chunks after
+    in-flight chunk j perturbed, chunks 0..j keep bitwise equal O and LSE."""
+    C, N, Hs, H, D = 6, 3, 2, 2, 8
+    q, k, v = (a.astype(np.float32) for a in _round_inputs(C, N, Hs, H, D, 23))
+
+    def run(q, k, v):
+        return Q.quantized_attention(q, k, v, Hs, C, 0.3, quant=quantize_round(q, k, Hs, C))
+
+    o, l = run(q, k, v)
+    for j in range(N - 1):
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        lo_q, lo_k = (j + 1) * C, (Hs + j + 1) * C
+        q2[lo_q:] = _rand(q2[lo_q:].shape, 77 + j, 3.0)
+        k2[lo_k:] = _rand(k2[lo_k:].shape, 177 + j, 3.0)
+        v2[lo_k:] = _rand(v2[lo_k:].shape, 277 + j, 3.0)
+        o2, l2 = run(q2, k2, v2)
+        assert np.array_equal(o2[:lo_q], o[:lo_q]), f"chunks 0..{j} changed"
+        assert np.array_equal(l2[:, :lo_q], l[:, :lo_q])
+        assert not np.allclose(o2[lo_q:], o[lo_q:])
+
+
+def test_int8_key_mean_golden():
+    check_kmean_golden(Q.quantize_round)
+
+
+def test_quantized_attention_is_chunk_causal():
+    check_quantized_causality(Q.quantize_round)
+
+
+def test_key_mean_input_errors():
+    with pytest.raises(ValueError):
+        Q.key_channel_mean(np.zeros((5, 1, 2), np.float32), 2, 2)
+
+
+def _with_key_mean(fn):
+    """Q.quantize_round with a planted key mean (the mutation tests below)."""
+    def quantize_round(q, k, Hs, C):
+        saved = Q.key_channel_mean
+        Q.key_channel_mean = fn
+        try:
+            return Q.quantize_round(q, k, Hs, C)
+        finally:
+            Q.key_channel_mean = saved
+    return quantize_round
+
+
+def _mean64(k, L):
+    return (np.asarray(k[:L], np.float64).sum(axis=0) / L).astype(np.float32)
+
+
+KMEAN_MUTANTS = {
+    "divisor_off_by_7": lambda k, Hs, C: (np.asarray(k[:(Hs + 1) * C], np.float64).sum(axis=0)
+                                          / ((Hs + 1) * C + 7)).astype(np.float32),
+    "all_keys": lambda k, Hs, C: _mean64(k, k.shape[0]),
+    "history_only": lambda k, Hs, C: _mean64(k, max(Hs, 1) * C),
+    "no_shift": lambda k, Hs, C: np.zeros(k.shape[1:], np.float32),
+    "refresh_chunk_only": lambda k, Hs, C: (np.asarray(k[Hs * C:(Hs + 1) * C], np.float64).mean(axis=0)
+                                            ).astype(np.float32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(KMEAN_MUTANTS))
+def test_key_mean_mutants_are_caught(name):
+    quantize_round = _with_key_mean(KMEAN_MUTANTS[name])
+    caught = False
+    for check in (check_kmean_golden, check_quantized_causality):
+        try:
+            check(quantize_round)
+        except AssertionError:
+            caught = True
+    assert caught, name
+
+
+def test_all_keys_mean_breaks_causality():
+    """The reading that takes the mean over every key of the round leaks later
+    chunks' keys into earlier chunks' codes: the causality pin itself sees it."""
+    with pytest.raises(AssertionError):
+        check_quantized_causality(_with_key_mean(KMEAN_MUTANTS["all_keys"]))
+
+
+def test_unmutated_key_mean_passes_the_checks():
+    quantize_round = _with_key_mean(Q.key_channel_mean)
+    check_kmean_golden(quantize_round)
+    check_quantized_causality(quantize_round)
 
 
 def test_quantized_attention_close_to_exact():
