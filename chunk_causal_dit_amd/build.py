@@ -29,18 +29,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False, jobs: int = 4, defines=(), out: str = LIB) -> str:
+def build(verbose: bool = False, jobs: int = 4, out: str = LIB) -> str:
     """Compile every source to an object, then link the library (libwf.so by
-    default). ``defines`` are extra -D flags (compile-time kernel variants).
-    Returns the library path."""
+    default). Returns the library path."""
     cc = hipcc()
-    tag = "_".join(d.replace("=", "") for d in defines)
-    obj_dir = os.path.join(HERE, "_build" + ("_" + tag if tag else ""))
+    obj_dir = os.path.join(HERE, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     common = [
         "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"-I{INCLUDE}", f"-I{CSRC}",
         "-Wall", "-Wno-unused-function",
-    ] + [f"-D{d}" for d in defines]
+    ]
     hip_flags = [
         f"--offload-arch={ARCH}", "-x", "hip",
         # no packed-FP32 instructions in device code

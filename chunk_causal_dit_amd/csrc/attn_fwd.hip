@@ -48,6 +48,11 @@ constexpr int KT = 64;  // keys per tile
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kTileSumMax = 256.0f;  // 2^kRescaleLog2
+// The int8 scores accumulate on top of kMagicI, the bits of the float kMagicF =
+// 1.5 * 2^23: for |score| < 2^22 (127 * 127 * 128 < 2^21) the int32 sum read as
+// a float is exactly kMagicF + score, so no int -> float conversion is needed.
+constexpr int kMagicI = 0x4B400000;
+constexpr float kMagicF = 12582912.0f;
 
 // A-operand row i of a 32-key block reads key key_of_arow(i). With the 32x32
 // output layout (lane half hh, element r <-> row 8*(r/4) + 4*hh + r%4) this
@@ -214,25 +219,9 @@ extern __shared__ __attribute__((aligned(1024))) char g_smem[];
 // t%3 from step t-2 to step t, V(t) in V stage t%3 from step t-1 to step t+1,
 // so no stage is overwritten while a wave can still read it.
 //
-// PINGPONG = true: waves 0-3 and 4-7 (one of each per SIMD) run half a step
-// apart, each half-step ending with a barrier, so that on every SIMD one wave
-// feeds the matrix cores while the other runs the softmax.
-#ifndef WF_ATTN_PINGPONG
-#define WF_ATTN_PINGPONG 1
-#endif
-#ifndef WF_ATTN_LDS_DEPTH
-#define WF_ATTN_LDS_DEPTH 4
-#endif
-#ifndef WF_ATTN_SETPRIO
-#define WF_ATTN_SETPRIO 0
-#endif
-#ifndef WF_ATTN_LEAD_GROUP
-#define WF_ATTN_LEAD_GROUP 1
-#endif
-// 1: the softmax skips the row max while the weights stay bounded (see vblock)
-#ifndef WF_ATTN_MAXFREE
-#define WF_ATTN_MAXFREE 1
-#endif
+// Ping-pong: waves 4-7 lead waves 0-3 (one of each per SIMD) by half a step,
+// each half-step ending with a barrier, so that on every SIMD one wave feeds
+// the matrix cores while the other runs the softmax.
 
 // I8 = true: the int8-QK variant. S^T = K'^T Q^T runs on int8 MFMA over the
 // codes that attn_i8qk.hip wrote (K - mean and Q, 128-token blocks); the wave's
@@ -247,9 +236,109 @@ struct TileBytes {
   static constexpr int LDS = 3 * K + 3 * V;
 };
 
-template <int D, int NW, bool PINGPONG, bool I8 = false>
+// int8-QK MFMA block of one step, written out with exact LDS waits: the 8
+// Q.K MFMAs of tile t (int8, scores start from kMagicI), then the 16 P.V MFMAs
+// of tile t-1 (bf16). Each MFMA's A operand is read from LDS four reads ahead,
+// and the wait before it lets the three later reads stay in flight (the
+// compiler's own waits drained all reads every fourth MFMA). The Q.K MFMAs go
+// first, so the scores are ready long before the block ends; the caller waits
+// out the MFMA-result hazard (mfma_to_valu) before the VALU touches o. The
+// leading s_nop covers VALU writes of P and O just before the block. Every
+// read is waited for inside the block.
+//   kaddr: LDS address of this lane's first K-code piece (stage + k_lane);
+//   vaddr: LDS address of this lane's first V piece (stage + v_lane).
+__device__ __forceinline__ void mblock_i8(f32x16 (&o)[4], i32x16 (&si)[2], const i32x4 (&qop8)[4],
+                                          const bf16x8 (&pk)[4], const i32x16& magic16, unsigned kaddr,
+                                          unsigned vaddr) {
+  bf16x8 abuf[4];
+  asm volatile(
+      "s_nop 3\n\t"
+      "ds_read_b128 %6, %18 offset:0\n\t"
+      "ds_read_b128 %7, %18 offset:512\n\t"
+      "ds_read_b128 %8, %18 offset:1024\n\t"
+      "ds_read_b128 %9, %18 offset:1536\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_i32_32x32x32_i8 %4, %6, %10, %20\n\t"
+      "ds_read_b128 %6, %18 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_i32_32x32x32_i8 %5, %7, %10, %20\n\t"
+      "ds_read_b128 %7, %18 offset:2560\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_i32_32x32x32_i8 %4, %8, %11, %4\n\t"
+      "ds_read_b128 %8, %18 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_i32_32x32x32_i8 %5, %9, %11, %5\n\t"
+      "ds_read_b128 %9, %18 offset:3584\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_i32_32x32x32_i8 %4, %6, %12, %4\n\t"
+      "ds_read_b128 %6, %19 offset:0\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_i32_32x32x32_i8 %5, %7, %12, %5\n\t"
+      "ds_read_b128 %7, %19 offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_i32_32x32x32_i8 %4, %8, %13, %4\n\t"
+      "ds_read_b128 %8, %19 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_i32_32x32x32_i8 %5, %9, %13, %5\n\t"
+      "ds_read_b128 %9, %19 offset:1536\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %14, %0\n\t"
+      "ds_read_b128 %6, %19 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %7, %14, %1\n\t"
+      "ds_read_b128 %7, %19 offset:4608\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %8, %14, %2\n\t"
+      "ds_read_b128 %8, %19 offset:5120\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %9, %14, %3\n\t"
+      "ds_read_b128 %9, %19 offset:5632\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %15, %0\n\t"
+      "ds_read_b128 %6, %19 offset:8192\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %7, %15, %1\n\t"
+      "ds_read_b128 %7, %19 offset:8704\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %8, %15, %2\n\t"
+      "ds_read_b128 %8, %19 offset:9216\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %9, %15, %3\n\t"
+      "ds_read_b128 %9, %19 offset:9728\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %16, %0\n\t"
+      "ds_read_b128 %6, %19 offset:12288\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %7, %16, %1\n\t"
+      "ds_read_b128 %7, %19 offset:12800\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %8, %16, %2\n\t"
+      "ds_read_b128 %8, %19 offset:13312\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %9, %16, %3\n\t"
+      "ds_read_b128 %9, %19 offset:13824\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %17, %0\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %7, %17, %1\n\t"
+      "s_waitcnt lgkmcnt(1)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %8, %17, %2\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %9, %17, %3\n\t"
+      : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "=&v"(si[0]), "=&v"(si[1]), "=&v"(abuf[0]), "=&v"(abuf[1]), "=&v"(abuf[2]), "=&v"(abuf[3])
+      : "v"(qop8[0]), "v"(qop8[1]), "v"(qop8[2]), "v"(qop8[3]), "v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]), "v"(kaddr), "v"(vaddr), "v"(magic16));
+}
+
+// The int8 MFMA block is inline asm, so the compiler does not know that its
+// last MFMAs write o: wait out the MFMA-result hazard before the VALU reads o.
+__device__ __forceinline__ void mfma_to_valu(f32x16 (&o)[4]) {
+  asm volatile("s_nop 15\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+}
+
+template <int D, int NW, bool I8 = false>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p) {
   static_assert(NW == 8, "8 waves: two per SIMD");
+  static_assert(!I8 || D == 128, "the int8 block is written for head_dim 128");
   using G = Geo<__bf16, D, NW>;
   using TB = TileBytes<D, I8>;
   constexpr int KS = D / 16;               // bf16 MFMA steps over head_dim (16 per step)
@@ -260,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
   const Work w = decode_work(blockIdx.x, p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = (wave >> 2) ^ WF_ATTN_LEAD_GROUP;  // group 0 leads by half a step
+  const int grp = (wave >> 2) ^ 1;  // group 0 (waves 4-7) leads by half a step
   const int qi = lane & 31, hh = lane >> 5;
   const int C = p.chunk_tokens, H = p.n_heads;
   const int wrow = w.qt * (NW * 32) + wave * 32;
@@ -357,7 +446,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
   f32x16 s[2];
-  i32x16 si[2];  // I8: integer scores
+  i32x16 si[2];  // I8: integer scores, biased by kMagicI
+  i32x16 magic16;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) magic16[e] = kMagicI;
   bf16x8 pk[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
@@ -373,7 +465,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
   // MFMA block with an explicit operand pipeline: LDS reads run DEPTH
   // operands ahead of the MFMAs in one straight-line region. Op i < NPV is a
   // P.V step (kk = i / DB, d = i % DB); op i >= NPV a Q.K step (k, b).
-  constexpr int DEPTH = WF_ATTN_LDS_DEPTH;
+  constexpr int DEPTH = 4;
   constexpr int NPV = 4 * DB, NQK = 2 * KSQ;
   auto mrun = [&](const char* vs, const char* ks, auto has_pv, auto has_qk) {
     constexpr bool PV = decltype(has_pv)::value, QK = decltype(has_qk)::value;
@@ -428,21 +520,23 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
   // computes scores that are never used. r = t % 3 is the K stage of tile t.
   auto mblock = [&](int r) {
     const int rv = r == 0 ? G::NSTAGE - 1 : r - 1;  // V stage of tile t-1
-    if (WF_ATTN_SETPRIO == 1) __builtin_amdgcn_s_setprio(1);  // the matrix-core feeder wins issue ties
-    mrun(vst(rv) + v_lane, kst(r) + k_lane, std::true_type{}, std::true_type{});
-    if (WF_ATTN_SETPRIO == 1) __builtin_amdgcn_s_setprio(0);
+    if constexpr (I8) {
+      mblock_i8(o, si, qop8, pk, magic16, (unsigned)(size_t)(LDS_AS char*)(kst(r) + k_lane),
+                (unsigned)(size_t)(LDS_AS char*)(vst(rv) + v_lane));
+    } else {
+      mrun(vst(rv) + v_lane, kst(r) + k_lane, std::true_type{}, std::true_type{});
+    }
   };
 
   // online softmax of a tile; kt = its index inside its chunk, cl its chunk
   auto vblock = [&](int kt, int cl) {
-    if (WF_ATTN_SETPRIO == 2) __builtin_amdgcn_s_setprio(1);
-    float ct = sl2e;  // log2-domain factor of the raw scores
+    float ct = sl2e;   // log2-domain factor of the raw scores
+    float bias = 0.f;  // I8: the float bias kMagicF of the integer scores
     if constexpr (I8) {
       ct *= ksc[cl * p.q_blocks + (kt >> 1)];
+      bias = kMagicF;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[b][e] = (float)si[b][e];  // |score| < 2^24: exact
+      for (int b = 0; b < 2; ++b) s[b] = __builtin_bit_cast(f32x16, si[b]);  // kMagicF + score, exactly
     }
     const int valid = min(KT, C - kt * KT);
     if (valid < KT) {  // zero padding past the chunk end takes no weight
@@ -453,9 +547,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
           if (32 * b + key_of_elem(hh, e) >= valid) s[b][e] = -INFINITY;
     }
     // Exact row max of the tile (four independent chains, then the other half of
-    // the row) and the lazy move of the reference max: the running output and
-    // sums are rescaled only when the tile max exceeds m_ref by kRescaleLog2.
-    auto move_max = [&](bool always) {
+    // the row) and the move of the reference max, with the running output and
+    // sums rescaled. The fast path below calls it only when a weight against the
+    // current m_ref could exceed 2^kRescaleLog2, so m_ref moves lazily.
+    auto move_max = [&]() {
       float m4[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -464,23 +559,22 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
         for (int e = 2; e < 8; ++e) m4[c] = fmaxf(m4[c], s[c >> 1][(c & 1) * 8 + e]);
       }
       float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-      const float tmax = mx * ct;
-      if (always || __builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleLog2)) {
-        const float mn = fmaxf(m_ref, tmax);
-        const float alpha = fast_exp2(m_ref - mn);
-        m_ref = mn;
+      const float tmax = (mx - bias) * ct;  // I8: exact subtraction (both in [2^23, 2^24))
+      const float mn = fmaxf(m_ref, tmax);
+      const float alpha = fast_exp2(m_ref - mn);
+      m_ref = mn;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) lsum[c] *= alpha;
+      for (int c = 0; c < 4; ++c) lsum[c] *= alpha;
+      if constexpr (I8) mfma_to_valu(o);
 #pragma unroll
-        for (int d = 0; d < DB; ++d)
+      for (int d = 0; d < DB; ++d)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-      }
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
     };
     // weights 2^(s ct - m_ref) rounded to bf16, and this lane's share of their sum
     // (the rounded weights actually used) in four accumulators
     auto weights = [&](float (&ts)[4]) {
-      const float nm = -m_ref;
+      const float nm = I8 ? fmaf(-bias, ct, -m_ref) : -m_ref;  // one rounding of the bias term
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -495,25 +589,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
         }
       }
     };
+    // Max-free fast path: weights against the current reference max. A lane's
+    // 32 weights summing to at most 2^kRescaleLog2 bound every weight by it, as
+    // the lazy move above would; a larger, infinite or NaN sum (the first tile,
+    // where m_ref = -inf, or a tile whose max moved up) takes the exact path.
     float ts[4];
-    if constexpr (WF_ATTN_MAXFREE) {
-      // Max-free fast path: weights against the current reference max. A lane's
-      // 32 weights summing to at most 2^kRescaleLog2 bound every weight by it, as
-      // the lazy move above would; a larger, infinite or NaN sum (the first tile,
-      // where m_ref = -inf, or a tile whose max moved up) takes the exact path.
-      weights(ts);
-      const float tl = (ts[0] + ts[1]) + (ts[2] + ts[3]);
-      if (__builtin_amdgcn_ballot_w64(!(tl <= kTileSumMax))) {
-        move_max(true);
-        weights(ts);
-      }
-    } else {
-      move_max(false);
+    weights(ts);
+    const float tl = (ts[0] + ts[1]) + (ts[2] + ts[3]);
+    if (__builtin_amdgcn_ballot_w64(!(tl <= kTileSumMax))) {
+      move_max();
       weights(ts);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) lsum[kk] += ts[kk];
-    if (WF_ATTN_SETPRIO == 2) __builtin_amdgcn_s_setprio(0);
   };
 
   // Copies started in step t: K(t+2) into K stage (t+2)%3, V(t+1) into V stage
@@ -541,21 +629,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
 
   if (!wave_on) {  // a wave past the chunk end still copies and meets every barrier
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
-      if (PINGPONG) lds_barrier();
+      lds_barrier();
       copies_and_wait(t, r);
     }
-  } else if (!PINGPONG || grp == 0) {
-    // in-phase order (and ping-pong group 0): M_t, [barrier], V_t, copies + barrier
+  } else if (grp == 0) {
+    // ping-pong group 0: M_t, barrier, V_t, copies + barrier
     int vkt = t_base % ktc, vcl = t_base / ktc;
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
       mblock(r);
-      if (PINGPONG) {
-        if constexpr (I8)
-          pin_scores(si[0], si[1]);
-        else
-          pin_scores(s[0], s[1]);
-        lds_barrier();
-      }
+      if constexpr (I8)
+        pin_scores(si[0], si[1]);
+      else
+        pin_scores(s[0], s[1]);
+      lds_barrier();
       if (t < n_iter) {
         vblock(vkt, vcl);
         if (++vkt == ktc) vkt = 0, ++vcl;
@@ -582,6 +668,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     }
   }
 
+  if constexpr (I8) mfma_to_valu(o);
   if (wave_on && w.part >= 0) {  // one half of a split query tile: unnormalized partials
     const float lt = halves_sum((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
     if (row_ok) {
@@ -826,9 +913,9 @@ hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& p, void* workspace
     // a split chunk 0 runs as two workgroups per query tile
     const int grid = (p.n_inflight + (p.split ? 1 : 0)) * kv.n_heads * p.q_tiles;
     hipError_t e = kv.head_dim == 128
-                       ? launch(attn_fwd_bf16_kernel<128, NW, WF_ATTN_PINGPONG>, TileBytes<128, false>::LDS, grid,
+                       ? launch(attn_fwd_bf16_kernel<128, NW>, TileBytes<128, false>::LDS, grid,
                                 NW * 64, p, s)
-                       : launch(attn_fwd_bf16_kernel<64, NW, WF_ATTN_PINGPONG>, TileBytes<64, false>::LDS, grid,
+                       : launch(attn_fwd_bf16_kernel<64, NW>, TileBytes<64, false>::LDS, grid,
                                 NW * 64, p, s);
     if (e != hipSuccess || !p.split) return e;
     const int blocks = (C * kv.n_heads + 3) / 4;  // one wave per (row, head) of chunk 0
@@ -860,7 +947,7 @@ hipError_t launch_attn_fwd_i8qk(const wf_kv_cache& kv, AttnParams& p, void* work
   p.key_tiles = (kv.chunk_tokens + KT - 1) / KT;
   p.q_tiles = (kv.chunk_tokens + NW * 32 - 1) / (NW * 32);
   const int grid = p.n_inflight * kv.n_heads * p.q_tiles;
-  return launch(attn_fwd_bf16_kernel<128, NW, WF_ATTN_PINGPONG, true>, lds, grid, NW * 64, p, s);
+  return launch(attn_fwd_bf16_kernel<128, NW, true>, lds, grid, NW * 64, p, s);
 }
 
 }  // namespace wf
