@@ -22,6 +22,10 @@ BF16_MEAN_REL = 5e-3
 # 3.4e-3 on every full-size round (p50 2.3e-3, from bf16 weights and the bf16 output);
 # one dropped or doubled 64-key tile moves a row of a 32,760-key round by about 4 %.
 BF16_ROW_REL = 6e-3
+# rounds whose Q and K are rotated (3D RoPE) on the GPU and stored in bf16 before attention,
+# while the oracle rotates in float64: one more bf16 rounding of every operand (measured at
+# most 8.4e-3 per row over the 20 long-rollout rounds, mean rel 3.3e-3)
+BF16_ROW_REL_ROPE = 1.2e-2
 F32_MAX_ABS = 1e-4
 
 
@@ -119,9 +123,9 @@ def row_rel_errors(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return d / np.maximum(np.abs(ref).sum(axis=-1), 1e-300)
 
 
-def assert_close(gpu_out, ref_out, dtype: str, what: str = "O"):
+def assert_close(gpu_out, ref_out, dtype: str, what: str = "O", row_rel: float = BF16_ROW_REL):
     """Aggregate bounds (max abs, mean relative error over all outputs) and, for
-    bf16, the per-row bound BF16_ROW_REL on every (row, head) of a [rows][H][D]
+    bf16, the per-row bound row_rel on every (row, head) of a [rows][H][D]
     output, so that one wrong row cannot hide in the aggregate."""
     mx, rel = error_stats(gpu_out, ref_out)
     msg = f"[parity] {what}: max abs {mx:.3e}, mean rel {rel:.3e}"
@@ -139,7 +143,7 @@ def assert_close(gpu_out, ref_out, dtype: str, what: str = "O"):
         assert rel <= BF16_MEAN_REL, f"{what}: mean rel {rel} > {BF16_MEAN_REL}"
         if rows is not None:
             worst = np.unravel_index(np.argmax(rows), rows.shape)
-            assert rows.max() <= BF16_ROW_REL, f"{what}: row {worst} rel {rows.max()} > {BF16_ROW_REL}"
+            assert rows.max() <= row_rel, f"{what}: row {worst} rel {rows.max()} > {row_rel}"
     return mx, rel
 
 

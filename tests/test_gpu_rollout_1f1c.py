@@ -51,7 +51,8 @@ def run_rollout(wf, S, F, W, C, H, D, dtype, seed, rows=None, check_rounds=None,
     for r, (o, l, inflight, hist) in got.items():
         ro_, rl_, plan = ref[r]
         assert inflight == plan["inflight"] and hist == plan["hist"]
-        RL.assert_close(o, ro_, dtype, f"round {r} ({len(inflight)} in flight, {len(hist)} history)")
+        RL.assert_close(o, ro_, dtype, f"round {r} ({len(inflight)} in flight, {len(hist)} history)",
+                        row_rel=RL.BF16_ROW_REL if rope is None else RL.BF16_ROW_REL_ROPE)
         assert np.abs(l - rl_).max() <= (1e-4 if dtype == "f32" else 2e-3)
     assert outputs == list(range(F))  # one output per round after the fill, in order
     return got
