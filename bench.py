@@ -472,7 +472,7 @@ def bench_power(torch, wf, cfg, seconds, split=True):
     return {"available": True, "watts": rec["watts"], "launches": launches, "ms_per_launch": s_per * 1e3,
             "joules_per_launch": rec["watts"] * s_per,
             "effective_gflop_per_joule": effective_flops(cfg) / (rec["watts"] * s_per) / 1e9,
-            "sensor": rec["sensor"]}
+            "clock_mhz": rec["clock_mhz"], "sensor": rec["sensor"], "clock_sensor": rec["clock_sensor"]}
 
 
 def copy_probe(torch, mib: int):
@@ -601,10 +601,18 @@ def main():
             "algorithmic_bytes_per_launch": attention_min_bytes(cfg),
             "timing": "hip events on the launch stream around each attention call (the attention kernel, plus the "
                       "merge kernel of the split), mean over the timed steps",
+            "call_avg_us": attn_s * 1e6,
         },
     }
     if args.power_seconds > 0:
         res["power"] = bench_power(torch, wf, cfg, args.power_seconds, split=split)
+        clk = res["power"].get("clock_mhz")
+        if clk:
+            # the shader clock the board ran this call at (hwmon, sampled during the power loop),
+            # and the dense bf16 peak at that clock: CUs x 4096 flop/clk x clock
+            clk_peak = n_cu * 4096 * clk * 1e6 / 1e12
+            res["roofline"].update({"clock_mhz": clk, "clock_peak_tflops": clk_peak,
+                                    "frac_of_clock_peak": achieved / clk_peak})
     if not args.no_extras:
         res["rollout"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream, split=split)
         res["rollout_fused"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream, fused=True,

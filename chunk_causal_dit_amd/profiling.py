@@ -96,19 +96,27 @@ def hwmon_power_paths() -> List[str]:
 def sample_power(run: Callable[[], None], sync: Callable[[], None], seconds: float = 3.0,
                  period: float = 0.01) -> Optional[dict]:
     """Calls run() repeatedly for about `seconds` (sync() after each call) while a thread reads
-    the board power sensor; returns mean watts (first quarter of the samples dropped as
-    ramp-up), calls made and wall seconds, or None when no sensor is readable."""
+    the board power sensor and, where the same hwmon directory has one, the shader clock
+    sensor (freq1_input, Hz); returns mean watts and mean clock in MHz (first quarter of the
+    samples dropped as ramp-up), calls made and wall seconds, or None when no power sensor
+    is readable."""
     paths = hwmon_power_paths()
     if not paths:
         return None
     path = paths[0]
+    clk_path = os.path.join(os.path.dirname(path), "freq1_input")
+    if not os.path.exists(clk_path):
+        clk_path = None
     samples: List[float] = []
+    clocks: List[float] = []
     stop = threading.Event()
 
     def sampler():
         while not stop.is_set():
             try:
                 samples.append(float(open(path).read()) * 1e-6)
+                if clk_path:
+                    clocks.append(float(open(clk_path).read()) * 1e-6)
             except (OSError, ValueError):
                 pass
             time.sleep(period)
@@ -126,7 +134,9 @@ def sample_power(run: Callable[[], None], sync: Callable[[], None], seconds: flo
     kept = samples[len(samples) // 4:]
     if not kept:
         return None
-    return {"watts": sum(kept) / len(kept), "calls": calls, "seconds": wall, "sensor": path}
+    ck = clocks[len(clocks) // 4:]
+    return {"watts": sum(kept) / len(kept), "clock_mhz": (sum(ck) / len(ck)) if ck else None, "calls": calls,
+            "seconds": wall, "sensor": path, "clock_sensor": clk_path}
 
 
 def main(argv=None):
