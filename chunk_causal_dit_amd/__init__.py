@@ -94,6 +94,7 @@ _SIGNATURES = {
     "wf_chunk_causal_attn_fwd": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp]),
     "wf_attn_fwd_workspace_bytes": (_c_size, [_vp]),
     "wf_chunk_causal_attn_fwd_ws": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp, _vp]),
+    "wf_chunk_causal_attn_fwd_static": (_c_int, [_vp, _vp, _c_int, ctypes.c_float, _vp, _vp, _vp]),
     "wf_kv_set_rope": (_c_int, [_vp] + [_c_int] * 6 + [ctypes.c_float]),
     "wf_kv_append_rope": (_c_int, [_vp, _vp, _vp, _c_int, _vp, ctypes.POINTER(_c_int)]),
     "wf_kv_refresh_rope": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _vp]),
@@ -340,6 +341,20 @@ def chunk_causal_attn_fwd(q: torch.Tensor, cache: KVCache, n_inflight: int, scal
         _check(lib().wf_chunk_causal_attn_fwd_ws(_dev(q, "q"), cache.handle, n_inflight, float(scale), ws,
                                                  _dev(out, "out"), lse_p, _vp(_stream(stream))),
                "wf_chunk_causal_attn_fwd_ws")
+    return out, lse
+
+
+def chunk_causal_attn_fwd_static(q: torch.Tensor, cache: KVCache, n_inflight: int, scale: float,
+                                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                                 with_lse: bool = True, stream=None):
+    """wf_chunk_causal_attn_fwd_static: the key-split call with its partials in the library's
+    static device scratch (the C call allocates nothing; out and lse are allocated here when
+    not given). Calls that overlap on one GPU race on the scratch. Returns (out, lse or None)."""
+    out, lse = _attn_io(q, cache, n_inflight, out, lse, with_lse)
+    _check(lib().wf_chunk_causal_attn_fwd_static(_dev(q, "q"), cache.handle, n_inflight, float(scale),
+                                                 _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
+                                                 _vp(_stream(stream))),
+           "wf_chunk_causal_attn_fwd_static")
     return out, lse
 
 

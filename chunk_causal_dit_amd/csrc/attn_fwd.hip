@@ -29,9 +29,17 @@
 //     the accumulators are rescaled only when a row's max grows by more than
 //     2^8, which keeps weights <= 256 and the result exact up to rounding.
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "wf_internal.h"
+
+// Scratch of the allocation-free call (wf_chunk_causal_attn_fwd_static): the
+// key-split partials live in this file-scope device array, one copy per GPU
+// the library runs on, held until the process ends. Host code never uses the
+// name itself (in host code it is a stand-in, not a device address): the
+// address comes from hipGetSymbolAddress, per device (wf::static_scratch).
+static __device__ __align__(256) char scratch[WF_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -889,6 +897,25 @@ hipError_t launch(Kern k, int lds, int grid, int block, const wf::AttnParams& p,
 }  // namespace
 
 namespace wf {
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // first call on this device, which is current: look its copy up once
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t attn_split_bytes(const wf_kv_cache& kv) {
   if (kv.dtype != WF_BF16) return 0;

@@ -348,6 +348,25 @@ WF_EXPORT int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, 
   return hip_status(launch_attn_fwd(*kv, p, workspace, static_cast<hipStream_t>(stream)), who);
 }
 
+WF_EXPORT int wf_chunk_causal_attn_fwd_static(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
+                                              void* out, float* lse, void* stream) {
+  const char* who = "wf_chunk_causal_attn_fwd_static";
+  AttnParams p;
+  int st = fill_attn_params(q, kv, n_inflight, scale, out, lse, p, who);
+  if (st != WF_OK) return st;
+  const size_t need = attn_split_bytes(*kv);
+  if (need > (size_t)WF_STATIC_SCRATCH_BYTES)
+    return fail(WF_E_SHAPE, "%s: the key-split partials of this cache need %zu bytes, more than the %zu-byte static "
+                "scratch (use wf_chunk_causal_attn_fwd_ws with a workspace)", who, need,
+                (size_t)WF_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need) {
+    const hipError_t e = static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, who);
+  }
+  return hip_status(launch_attn_fwd(*kv, p, ws, static_cast<hipStream_t>(stream)), who);
+}
+
 WF_EXPORT size_t wf_attn_i8qk_workspace_bytes(const wf_kv_cache* kv, int n_inflight) {
   if (!kv || n_inflight < 1 || n_inflight > (int)kv->table.size()) return 0;
   if (kv->dtype != WF_BF16 || kv->head_dim != 128) return 0;

@@ -107,6 +107,9 @@ struct AttnParams {
   int slots[WF_MAX_TABLE];  // physical slot of logical chunk c = 0..n_hist+n_inflight-1
 };
 
+// Device address of the current device's WF_STATIC_SCRATCH_BYTES-byte static scratch
+// (looked up on the first call on each device, with that device current).
+hipError_t static_scratch(void** ptr);
 // workspace: NULL, or attn_split_bytes(kv) bytes (256-byte aligned) that enable the key split
 hipError_t launch_attn_fwd(const wf_kv_cache& kv, AttnParams& prm, void* workspace, hipStream_t s);
 // Bytes of the key-split partials of a bf16 cache (0 for fp32 caches, which never split).

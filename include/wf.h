@@ -212,6 +212,27 @@ size_t wf_attn_fwd_workspace_bytes(const wf_kv_cache* kv); /* 0 for fp32 caches 
 int wf_chunk_causal_attn_fwd_ws(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
                                 void* workspace, void* out, float* lse, void* stream);
 
+/* Allocation-free form of wf_chunk_causal_attn_fwd_ws, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the key-split partials live in a static
+ * device array of WF_STATIC_SCRATCH_BYTES bytes inside the library instead of
+ * a caller's workspace. Same result, bitwise, as wf_chunk_causal_attn_fwd_ws
+ * with a workspace. The caller still passes q, out and lse; the call itself
+ * allocates nothing (no hipMalloc, no hipFree). Each GPU the library runs on
+ * holds its own copy of the array until the process ends. Every call on one
+ * GPU shares that GPU's copy: calls that overlap on one GPU (concurrent
+ * streams, or host threads without ordering) race on it and must be ordered
+ * on one stream. Nothing in it needs to start at zero (each call writes all it
+ * reads) and it keeps the last call's partials.
+ * Errors: those of wf_chunk_causal_attn_fwd; WF_E_SHAPE when the cache's
+ * partials (wf_attn_fwd_workspace_bytes, about 8 n_heads chunk_tokens
+ * (head_dim + 2) bytes) exceed WF_STATIC_SCRATCH_BYTES (64 MiB): 4680-token
+ * chunks of head_dim 128 fit up to 13 heads, 14 heads do not. fp32 caches
+ * never split and use no scratch. */
+#define WF_STATIC_SCRATCH_BYTES (64ull << 20)
+int wf_chunk_causal_attn_fwd_static(const void* q, const wf_kv_cache* kv, int n_inflight, float scale,
+                                    void* out, float* lse, void* stream);
+
 /* ------------------------------------------------------------------------
  * int8-QK variant (bf16 caches, head_dim 128). The pages name a
  * quantized-QK attention backend (SageAttention) in their DiT-only tests

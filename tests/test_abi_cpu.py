@@ -54,7 +54,7 @@ def test_exports_match_header(L):
     declared = wf.header_symbols()
     exported = wf.exported_symbols()
     assert declared == exported, (sorted(set(declared) - set(exported)), sorted(set(exported) - set(declared)))
-    assert len(declared) == 26
+    assert len(declared) == 27
 
 
 def test_device_peak_info_argument_errors(L):
@@ -188,6 +188,30 @@ def test_attention_argument_errors(L):
     assert g(q, h32, 2, 0.1, ws, q, lse, None) == WF_E_DTYPE
     assert L.wf_attn_fwd_workspace_bytes(h32) == 0  # fp32 rounds never split
     L.wf_kv_cache_destroy(h32)
+
+
+def test_static_scratch_call_refuses_before_any_launch(L):
+    """wf_chunk_causal_attn_fwd_static: the attention call's argument checks, and a cache
+    whose key-split partials exceed the 64 MiB static scratch refused with WF_E_SHAPE."""
+    fs = L.wf_chunk_causal_attn_fwd_static
+    h, pools = make_cache(L, n_slots=4)
+    q = ctypes.c_void_p(pools.k.value)
+    assert fs(None, h, 1, 0.1, q, None, None) == WF_E_NULL
+    assert fs(q, None, 1, 0.1, q, None, None) == WF_E_NULL
+    assert fs(q, h, 1, 0.1, q, None, None) == WF_E_EMPTY
+    assert set_table(L, h, [2, 0, 1]) == WF_OK
+    assert fs(q, h, 4, 0.1, q, None, None) == WF_E_EMPTY
+    assert fs(q, h, 2, 0.0, q, None, None) == WF_E_SHAPE
+    L.wf_kv_cache_destroy(h)
+    # 14 heads of 4680 tokens, head_dim 128: 2 x 14 x 4680 x (4 x 128 + 8) bytes > 64 MiB
+    big, bp = make_cache(L, n_slots=3, C=4680, H=14, D=128)
+    assert set_table(L, big, [0, 1, 2]) == WF_OK
+    need = L.wf_attn_fwd_workspace_bytes(big)
+    assert need > 64 << 20
+    st = fs(ctypes.c_void_p(bp.k.value), big, 2, 0.1, ctypes.c_void_p(bp.k.value), None, None)
+    assert st == WF_E_SHAPE and b"static" in L.wf_last_error()
+    assert table(L, big) == [0, 1, 2]
+    L.wf_kv_cache_destroy(big)
 
 
 def test_workspace_overlap_refused(L):
