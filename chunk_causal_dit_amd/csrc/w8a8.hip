@@ -104,9 +104,7 @@ constexpr int NST = 3;                      // LDS stages
 constexpr int TILE_A = BM * BK, TILE_B = BN * BK;
 constexpr int STAGE = TILE_A + TILE_B;      // 32 KB
 constexpr int LDS_MAIN = NST * STAGE;
-constexpr int OUT_LD = BN + 4;              // bf16 staging row stride (elements): 520 bytes, so the
-                                            // 32 rows of one 8-byte write hit 32 different bank pairs
-constexpr int LDS_OUT = BM * OUT_LD * 2;
+constexpr int LDS_OUT = BM * (BN + 4) * 2;  // bf16 staging of a 256 x 256 tile (see gemm_epilogue)
 constexpr int LDS_BYTES = LDS_OUT > LDS_MAIN ? LDS_OUT : LDS_MAIN;
 constexpr int COPIES = 2 * (BM / 16) / NWV;  // copy instructions per wave per stage (A and B)
 static_assert(BM == BN, "copy_rows serves both operands");
@@ -141,6 +139,7 @@ template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else static_assert(N == 0, "unsupported wait count");
@@ -162,15 +161,19 @@ __device__ __forceinline__ void tile_of(int b, int tm_count, int tn_count, int& 
   tn = in / rows;
 }
 
-// Epilogue of a 256 x 256 tile held as acc[i][j] by 4 waves (layout as in the kernels
-// below): the raw int32 accumulators, or the fp32 scale/bias step rounded to bf16,
-// staged through LDS and stored as 16-byte row pieces. The tile's LDS stages must no
-// longer be read when it starts.
-template <bool OUT_I32>
-__device__ __forceinline__ void gemm_epilogue(const i32x16 (&acc)[4][4], char* lds, const float* __restrict__ sx,
-                                              const float* __restrict__ sw, const __bf16* __restrict__ bias, int M,
-                                              int N, int m0, int n0, int wm, int wn, int rr, int hh, int tid,
-                                              void* __restrict__ y) {
+// Epilogue of a 256 x TN tile held as acc[i][j] by 4 waves (2 x 2, each 128 x TN/2; layout
+// as in the kernels below): the raw int32 accumulators, or the fp32 scale/bias step
+// rounded to bf16, staged through LDS and stored as 16-byte row pieces. The tile's LDS
+// stages must no longer be read when it starts.
+template <bool OUT_I32, int TN>
+__device__ __forceinline__ void gemm_epilogue(const i32x16 (&acc)[4][TN / 64], char* lds,
+                                              const float* __restrict__ sx, const float* __restrict__ sw,
+                                              const __bf16* __restrict__ bias, int M, int N, int m0, int n0, int wm,
+                                              int wn, int rr, int hh, int tid, void* __restrict__ y) {
+  constexpr int JB = TN / 64;     // 32-column blocks per wave
+  constexpr int LD = TN + 4;      // staging row stride (elements): LD / 2 dwords is 2 mod 4, so the
+                                  // 32 rows of one 8-byte write land on 32 different bank pairs
+  static_assert((LD / 2) % 4 == 2, "staging stride");
   if constexpr (OUT_I32) {
     int* yo = static_cast<int*>(y);
 #pragma unroll
@@ -178,10 +181,10 @@ __device__ __forceinline__ void gemm_epilogue(const i32x16 (&acc)[4][4], char* l
       const int m = m0 + wm * 128 + 32 * i + rr;
       if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JB; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 128 + 32 * j + 8 * g + 4 * hh;
+          const int n = n0 + wn * (TN / 2) + 32 * j + 8 * g + 4 * hh;
           if (n < N)
             *reinterpret_cast<i32x4*>(yo + (size_t)m * N + n) =
                 i32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
@@ -189,16 +192,16 @@ __device__ __forceinline__ void gemm_epilogue(const i32x16 (&acc)[4][4], char* l
     }
     return;
   }
-  // fp32 epilogue into the bf16 staging tile [BM][OUT_LD] (the stages are no longer read)
+  // fp32 epilogue into the bf16 staging tile [BM][LD] (the stages are no longer read)
   __bf16* out_lds = reinterpret_cast<__bf16*>(lds);
   float sxm[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) sxm[i] = sx[min(m0 + wm * 128 + 32 * i + rr, M - 1)];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < JB; ++j)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int nl = wn * 128 + 32 * j + 8 * g + 4 * hh;
+      const int nl = wn * (TN / 2) + 32 * j + 8 * g + 4 * hh;
       float swn[4], bn[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -212,19 +215,19 @@ __device__ __forceinline__ void gemm_epilogue(const i32x16 (&acc)[4][4], char* l
         __bf16 v[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[c] = (__bf16)fmaf((float)acc[i][j][4 * g + c], sxm[i] * swn[c], bn[c]);
-        *reinterpret_cast<uint2*>(out_lds + ml * OUT_LD + nl) = *reinterpret_cast<const uint2*>(v);
+        *reinterpret_cast<uint2*>(out_lds + ml * LD + nl) = *reinterpret_cast<const uint2*>(v);
       }
     }
   __syncthreads();
   // coalesced stores: 16-byte pieces (8 columns) of each row
   __bf16* yo = static_cast<__bf16*>(y);
-  constexpr int PIECES = BM * BN / 8;
+  constexpr int PIECES = BM * TN / 8;
 #pragma unroll 4
   for (int idx = tid; idx < PIECES; idx += NWV * 64) {
-    const int rl = idx / (BN / 8), cp = idx % (BN / 8);
+    const int rl = idx / (TN / 8), cp = idx % (TN / 8);
     const int m = m0 + rl, n = n0 + cp * 8;
     if (m < M && n < N) {
-      const uint2* src = reinterpret_cast<const uint2*>(out_lds + rl * OUT_LD + cp * 8);  // 8-byte aligned
+      const uint2* src = reinterpret_cast<const uint2*>(out_lds + rl * LD + cp * 8);  // 8-byte aligned
       const uint2 lo = src[0], hi = src[1];
       *reinterpret_cast<u32x4*>(yo + (size_t)m * N + n) = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
@@ -339,20 +342,28 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
   for (; kt < KT; ++kt, s = s == NST - 1 ? 0 : s + 1) body(std::false_type{}, kt, s);
   __syncthreads();
 
-  gemm_epilogue<OUT_I32>(acc, lds, sx, sw, bias, M, N, m0, n0, wm, wn, rr, hh, tid, y);
+  gemm_epilogue<OUT_I32, BN>(acc, lds, sx, sw, bias, M, N, m0, n0, wm, wn, rr, hh, tid, y);
 }
 
 // ---------------------------------------------------------------- GEMM, 128-byte K stages
-// Same tile, waves and epilogue as above, with K advancing 128 bytes per stage through
-// two 64 KB LDS stages: one barrier per 64 MFMAs of a wave instead of per 32. LDS rows
-// are 128 bytes (eight 16-byte pieces); piece p of row r sits in slot p ^ ((r >> 1) & 7),
-// which keeps the 16 lanes of each operand read on 16 different bank groups.
+// Same waves and epilogue as above, tiles 256 x TN (TN = 256 or 192: 4 waves of 128 x TN/2),
+// with K advancing 128 bytes per stage through two LDS stages: one barrier per 16 TN/64
+// MFMAs of a wave instead of per 32. LDS rows are 128 bytes (eight 16-byte pieces); piece p
+// of row r sits in slot p ^ ((r >> 1) & 7), which keeps the 16 lanes of each operand read
+// on 16 different bank groups. The 192-column tile is for shapes whose 256-column tiles
+// leave the last wave of workgroups mostly empty (it is picked per launch).
 constexpr int BK2 = 128;
-constexpr int TILE_A2 = BM * BK2, TILE_B2 = BN * BK2;
-constexpr int STAGE2 = TILE_A2 + TILE_B2;  // 64 KB
-constexpr int LDS2_MAIN = 2 * STAGE2;
-constexpr int LDS2_BYTES = LDS_OUT > LDS2_MAIN ? LDS_OUT : LDS2_MAIN;
-static_assert(LDS2_BYTES <= 160 * 1024, "LDS");
+constexpr int TILE_A2 = BM * BK2;
+template <int TN>
+struct K128 {
+  static constexpr int JB = TN / 64;                  // 32-column MFMA blocks per wave
+  static constexpr int TILE_B = TN * BK2;
+  static constexpr int STAGE = TILE_A2 + TILE_B;      // 64 KB (256) or 56 KB (192)
+  static constexpr int OUT = BM * (TN + 4) * 2;
+  static constexpr int LDS = OUT > 2 * STAGE ? OUT : 2 * STAGE;
+  static constexpr int BCOPY = TN / 8 / NWV;          // B copy instructions per wave per stage
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
 
 __device__ __forceinline__ int slot2_of(int r, int p) { return p ^ ((r >> 1) & 7); }
 
@@ -368,14 +379,16 @@ __device__ __forceinline__ void copy2_piece(const signed char* src, int rows, in
   __builtin_amdgcn_global_load_lds(src + (size_t)gr * K + k0 + p * 16, (LDS_AS void*)(lds + j * 1024), 16, 0, 0);
 }
 
-template <bool OUT_I32>
+template <bool OUT_I32, int TN>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w8a8_k128_kernel(
     const signed char* __restrict__ xq, const float* __restrict__ sx, const signed char* __restrict__ wq,
     const float* __restrict__ sw, const __bf16* __restrict__ bias, int M, int N, int K, void* __restrict__ y) {
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  using T = K128<TN>;
+  constexpr int JB = T::JB, STAGE2 = T::STAGE;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TN - 1) / TN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -387,53 +400,54 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int u = 0; u < 8; ++u) copy2_piece(xq, M, m0, K, kt * BK2, st, wave, lane, u);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) copy2_piece(wq, N, n0, K, kt * BK2, st + TILE_A2, wave, lane, u);
+    for (int u = 0; u < T::BCOPY; ++u) copy2_piece(wq, N, n0, K, kt * BK2, st + TILE_A2, wave, lane, u);
   };
-  // operand rows: A row wm*128 + 32i + rr, B row wn*128 + 32j + rr; k32 step ks takes piece
+  // operand rows: A row wm*128 + 32i + rr, B row wn*TN/2 + 32j + rr; k32 step ks takes piece
   // 2ks + hh; block i (j) adds 32 rows = 4096 bytes
   const int x = (rr >> 1) & 7;
   int aoff[4], boff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     aoff[ks] = (wm * 128 + rr) * BK2 + 16 * ((2 * ks + hh) ^ x);
-    boff[ks] = TILE_A2 + (wn * 128 + rr) * BK2 + 16 * ((2 * ks + hh) ^ x);
+    boff[ks] = TILE_A2 + (wn * (TN / 2) + rr) * BK2 + 16 * ((2 * ks + hh) ^ x);
   }
-  i32x4 a0[4], b0[4], a1[4], b1[4];
-  // one read of operand q (0..7, in the order the MFMAs use them: a[0], b[0..3], a[1..3])
-  auto read_op = [&](const char* st, int ks, int q, i32x4(&av)[4], i32x4(&bv)[4]) {
+  constexpr int NOPS = 4 + JB;  // operand reads per k32 step
+  i32x4 a0[4], b0[JB], a1[4], b1[JB];
+  // one read of operand q (0..NOPS-1, in the order the MFMAs use them: a[0], b[0..JB-1], a[1..3])
+  auto read_op = [&](const char* st, int ks, int q, i32x4(&av)[4], i32x4(&bv)[JB]) {
     if (q == 0) av[0] = *reinterpret_cast<const i32x4*>(st + aoff[ks]);
-    else if (q < 5) bv[q - 1] = *reinterpret_cast<const i32x4*>(st + boff[ks] + 4096 * (q - 1));
-    else av[q - 4] = *reinterpret_cast<const i32x4*>(st + aoff[ks] + 4096 * (q - 4));
+    else if (q <= JB) bv[q - 1] = *reinterpret_cast<const i32x4*>(st + boff[ks] + 4096 * (q - 1));
+    else av[q - JB] = *reinterpret_cast<const i32x4*>(st + aoff[ks] + 4096 * (q - JB));
   };
-  i32x16 acc[4][4];
+  i32x16 acc[4][JB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-  auto mfma_t = [&](int t, const i32x4(&av)[4], const i32x4(&bv)[4]) {
-    acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv[t & 3], av[t >> 2], acc[t >> 2][t & 3], 0, 0, 0);
+  auto mfma_t = [&](int t, const i32x4(&av)[4], const i32x4(&bv)[JB]) {
+    acc[t / JB][t % JB] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv[t % JB], av[t / JB], acc[t / JB][t % JB], 0, 0, 0);
   };
-  // a k32 step: 16 MFMAs on (av, bv), the first 8 each followed by one read of the next
-  // step's operands into (nav, nbv)
-  auto step = [&](const i32x4(&av)[4], const i32x4(&bv)[4], const char* nst, int nks, i32x4(&nav)[4],
-                  i32x4(&nbv)[4]) {
+  // a k32 step: 4 JB MFMAs on (av, bv), the first NOPS each followed by one read of the
+  // next step's operands into (nav, nbv)
+  auto step = [&](const i32x4(&av)[4], const i32x4(&bv)[JB], const char* nst, int nks, i32x4(&nav)[4],
+                  i32x4(&nbv)[JB]) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < 4 * JB; ++t) {
       mfma_t(t, av, bv);
-      if (t < 8) read_op(nst, nks, t, nav, nbv);
+      if (t < NOPS) read_op(nst, nks, t, nav, nbv);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   copy_stage(0, lds);
   if (KT > 1) copy_stage(1, lds + STAGE2);
-  if (KT > 1) wait_vm_barrier<16>();
+  if (KT > 1) wait_vm_barrier<8 + T::BCOPY>();
   else wait_vm_barrier<0>();
 #pragma unroll
-  for (int q = 0; q < 8; ++q) read_op(lds, 0, q, a0, b0);
+  for (int q = 0; q < NOPS; ++q) read_op(lds, 0, q, a0, b0);
 
   // Stage kt in buffer s: steps 0-2 each read the next step's operands; the barrier
   // (stage kt+1 has landed, every wave's reads of stage kt are done) comes before step 3,
@@ -452,33 +466,49 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1))
     if constexpr (decltype(full)::value) {
       char* cst = lds + s * STAGE2;
       __builtin_amdgcn_sched_barrier(0);
+      // slot t: MFMA t, then the next stage's read t (t < NOPS), the refill copies of A
+      // (t < 8) and of B (the last BCOPY slots)
+      constexpr int B0 = 4 * JB - T::BCOPY;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 4 * JB; ++t) {
         mfma_t(t, a1, b1);
-        if (t < 8) read_op(nst, 0, t, a0, b0);
+        if (t < NOPS) read_op(nst, 0, t, a0, b0);
         if (t < 8) copy2_piece(xq, M, m0, K, (kt + 2) * BK2, cst, wave, lane, t);
-        else copy2_piece(wq, N, n0, K, (kt + 2) * BK2, cst + TILE_A2, wave, lane, t - 8);
+        if (t >= B0) copy2_piece(wq, N, n0, K, (kt + 2) * BK2, cst + TILE_A2, wave, lane, t - B0);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       if (kt + 1 < KT) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) read_op(nst, 0, q, a0, b0);
+        for (int q = 0; q < NOPS; ++q) read_op(nst, 0, q, a0, b0);
       }
 #pragma unroll
-      for (int t = 0; t < 16; ++t) mfma_t(t, a1, b1);
+      for (int t = 0; t < 4 * JB; ++t) mfma_t(t, a1, b1);
     }
   };
   int kt = 0, s = 0;
   for (; kt + 2 < KT; ++kt, s ^= 1) body(std::true_type{}, kt, s);
   for (; kt < KT; ++kt, s ^= 1) body(std::false_type{}, kt, s);
   __syncthreads();
-  gemm_epilogue<OUT_I32>(acc, lds, sx, sw, bias, M, N, m0, n0, wm, wn, rr, hh, tid, y);
+  gemm_epilogue<OUT_I32, TN>(acc, lds, sx, sw, bias, M, N, m0, n0, wm, wn, rr, hh, tid, y);
 }
 
 }  // namespace
 
 namespace wf {
+
+bool use_narrow_tiles(int M, int N) {
+  // Modelled time in units of one 256 x 256 tile: waves of workgroups (one per CU) times
+  // the tile's width share, with the narrow tile's measured 10 % lower efficiency per unit
+  // of work (shorter MFMA runs per operand read, fixed per-tile prologue and epilogue).
+  // Measured on the Wan2.1 projections (23,400 tokens): the 1.3B O projection (552 wide
+  // tiles = 2.2 waves) gains 96 -> 82 us; the 14B O projection (7.2 waves) would lose 4 %.
+  constexpr int kCUs = 256;
+  const long long tm = (M + BM - 1) / BM;
+  const long long w256 = (tm * ((N + 255) / 256) + kCUs - 1) / kCUs;
+  const long long w192 = (tm * ((N + 191) / 192) + kCUs - 1) / kCUs;
+  return (double)w192 * 0.75 * 1.10 <= (double)w256;
+}
 
 hipError_t launch_quant_rows_i8(const void* x, int rows, int cols, void* q, float* scales, hipStream_t s) {
   const int pieces = (cols + 511) / 512;
@@ -511,16 +541,21 @@ hipError_t launch_gemm_w8a8(const void* xq, const float* sx, const void* wq, con
     return hipGetLastError();
   };
   if (K % BK2 == 0) {  // 128-byte stages: half the barriers per MFMA
-    auto run2 = [&](auto kern) {
+    const bool narrow = use_narrow_tiles(M, N);
+    auto run2 = [&](auto kern, int tn, int lds) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, LDS2_BYTES);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
-      kern<<<blocks, NWV * 64, LDS2_BYTES, s>>>(static_cast<const signed char*>(xq), sx,
-                                                 static_cast<const signed char*>(wq), sw,
-                                                 static_cast<const __bf16*>(bias), M, N, K, y);
+      const int nb = ((M + BM - 1) / BM) * ((N + tn - 1) / tn);
+      kern<<<nb, NWV * 64, lds, s>>>(static_cast<const signed char*>(xq), sx, static_cast<const signed char*>(wq),
+                                     sw, static_cast<const __bf16*>(bias), M, N, K, y);
       return hipGetLastError();
     };
-    return out_i32 ? run2(gemm_w8a8_k128_kernel<true>) : run2(gemm_w8a8_k128_kernel<false>);
+    if (narrow)
+      return out_i32 ? run2(gemm_w8a8_k128_kernel<true, 192>, 192, K128<192>::LDS)
+                     : run2(gemm_w8a8_k128_kernel<false, 192>, 192, K128<192>::LDS);
+    return out_i32 ? run2(gemm_w8a8_k128_kernel<true, 256>, 256, K128<256>::LDS)
+                   : run2(gemm_w8a8_k128_kernel<false, 256>, 256, K128<256>::LDS);
   }
   return out_i32 ? run(gemm_w8a8_kernel<true>) : run(gemm_w8a8_kernel<false>);
 }

@@ -119,6 +119,8 @@ size_t attn_split_bytes(const wf_kv_cache& kv);
 hipError_t launch_quant_rows_i8(const void* x, int rows, int cols, void* q, float* scales, hipStream_t s);
 hipError_t launch_gemm_w8a8(const void* xq, const float* sx, const void* wq, const float* sw, const void* bias, int M,
                             int N, int K, bool out_i32, void* y, hipStream_t s);
+// Whether a W8A8 GEMM of this shape (K % 128 == 0) runs on 256 x 192 tiles instead of 256 x 256.
+bool use_narrow_tiles(int M, int N);
 
 // ---- int8-QK path ----
 struct I8Layout {

@@ -97,6 +97,41 @@ def test_qkv_shape_sampled_rows():
     assert (np.abs(got - ref) <= BF16_REL * np.abs(ref) + 1e-6).all()
 
 
+def _narrow_tiles(M, N):
+    """The launch rule of the 128-byte-stage GEMM (w8a8.hip): 256 x 192 tiles when their
+    waves of workgroups, weighted by the tile width and a 10 % efficiency penalty, cost no
+    more than 256 x 256 tiles'."""
+    tm = -(-M // 256)
+    w256 = -(-(tm * -(-N // 256)) // 256)
+    w192 = -(-(tm * -(-N // 192)) // 256)
+    return w192 * 0.75 * 1.10 <= w256
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (23400, 1536, 1536), (700, 200, 384)])
+def test_tile_widths_sampled_rows(M, N, K):
+    """Both tile widths of the 128-byte-stage GEMM: 4096 x 4096 runs on 256 x 256 tiles, the
+    Wan2.1-1.3B O projection (23400 x 1536 x 1536) and a ragged small shape on 256 x 192
+    tiles. int32 accumulators bit-exact and bf16 outputs within rounding on sampled rows
+    (every column, so every column tile and the ragged last one are checked)."""
+    wf = RL.require_gpu()
+    print(f"[case] gemm M={M} N={N} K={K} narrow={_narrow_tiles(M, N)}", flush=True)
+    assert _narrow_tiles(M, N) == (N != 4096)
+    x, w, b = make_linear_inputs(M, N, K, seed=M + N + K)
+    xq, sx, wq, sw = _quantized(wf, x, w)
+    y = wf.gemm_w8a8(xq, sx, wq, sw, _dev(b, torch.bfloat16))
+    acc = wf.gemm_w8a8(xq, None, wq, None, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    rows = RL.boundary_rows(M, 1, 48, seed=5)
+    rows = rows[rows < M]
+    rq, rsx = OW.quantize_rows(x[rows])
+    wq_ref, rsw = OW.quantize_rows(w)
+    sel = torch.from_numpy(rows).cuda()
+    assert np.array_equal(acc[sel].cpu().numpy().astype(np.int64), OW.int8_matmul(rq, wq_ref))
+    ref = OW.w8a8_linear(rq, rsx, wq_ref, rsw, b)
+    got = y[sel].float().cpu().numpy()
+    assert (np.abs(got - ref) <= BF16_REL * np.abs(ref) + 1e-6).all()
+
+
 def test_deterministic_and_bias_optional():
     wf = RL.require_gpu()
     x, w, b = make_linear_inputs(300, 520, 1536, seed=12)
