@@ -47,7 +47,7 @@ I8QK_MIXED_PEAK = 1.0 / (0.5 / INT8_DENSE_TOPS + 0.5 / BF16_DENSE_TFLOPS)
 METRIC = "effective attention TFLOP/s per 1F1C round (% bf16 MFMA peak); chunk-rounds/s"
 PROFILES = os.path.join(ROOT, "profiles")
 ATTN_SRC = os.path.join(ROOT, "chunk_causal_dit_amd", "csrc", "attn_fwd.hip")
-ATTN_KERNEL = "attn_fwd_bf16_kernel<128, 8, true, false>"
+ATTN_KERNEL = "attn_fwd_bf16_kernel<128, 8, false>"
 MERGE_KERNEL = "attn_combine_kernel<128>"
 
 
@@ -278,8 +278,9 @@ def bench_rollout(torch, wf, cfg, rounds, warmup, stream, fused=False, split=Tru
     }
 
 
-def bench_i8qk(torch, wf, cfg, steps, warmup, stream):
-    """14B-shaped int8-QK round: quantization kernels + int8 attention, one C call."""
+def bench_i8qk(torch, wf, cfg, steps, warmup, stream, power_seconds=0.0):
+    """14B-shaped int8-QK round: quantization kernels + int8 attention, one C call (with
+    power_seconds > 0, also the board power, clock and energy per call back to back)."""
     C, H, D, N, Hs = cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, cfg.n_inflight, cfg.n_hist
     inp = make_round_inputs(cfg)
     q = dev_bf16(torch, inp.q)
@@ -306,7 +307,7 @@ def bench_i8qk(torch, wf, cfg, steps, warmup, stream):
     ms = np.array([t.ms(0, 1) for t in timers])
     eff = effective_flops(cfg)
     tops = eff / (np.median(ms) / 1e3) / 1e12
-    return {
+    res = {
         "workload": f"{cfg.name}: {cfg.description}",
         "call": "key sums, key mean, quantize K - mean and Q (4 kernels) + int8-QK attention",
         **ms_summary(ms),
@@ -316,6 +317,19 @@ def bench_i8qk(torch, wf, cfg, steps, warmup, stream):
         "frac_of_bf16_peak": tops / BF16_DENSE_TFLOPS,
         "chunk_rounds_per_s": 1e3 / float(np.median(ms)),
     }
+    if power_seconds > 0:
+        from chunk_causal_dit_amd.profiling import sample_power
+
+        def run():
+            for _ in range(5):
+                wf.chunk_causal_attn_fwd_i8qk(q, cache, N, cfg.scale, workspace=ws, out=out, lse=lse)
+
+        rec = sample_power(run, torch.cuda.synchronize, power_seconds)
+        if rec is not None:
+            s_per = rec["seconds"] / (rec["calls"] * 5)
+            res["power"] = {"watts": rec["watts"], "cap_watts": rec["cap_watts"], "clock_mhz": rec["clock_mhz"],
+                            "ms_per_call": s_per * 1e3, "joules_per_call": rec["watts"] * s_per}
+    return res
 
 
 # Linear shapes of the DiT blocks around attention: (name, out features, in features).
@@ -472,7 +486,8 @@ def bench_power(torch, wf, cfg, seconds, split=True):
     return {"available": True, "watts": rec["watts"], "launches": launches, "ms_per_launch": s_per * 1e3,
             "joules_per_launch": rec["watts"] * s_per,
             "effective_gflop_per_joule": effective_flops(cfg) / (rec["watts"] * s_per) / 1e9,
-            "clock_mhz": rec["clock_mhz"], "sensor": rec["sensor"], "clock_sensor": rec["clock_sensor"]}
+            "clock_mhz": rec["clock_mhz"], "cap_watts": rec["cap_watts"], "sensor": rec["sensor"],
+            "clock_sensor": rec["clock_sensor"]}
 
 
 def copy_probe(torch, mib: int):
@@ -532,7 +547,8 @@ def main():
         print(json.dumps({"w8a8": bench_w8a8(torch, wf, cfg.nq, args.steps, args.warmup, stream)}), flush=True)
         return
     if args.i8qk_only:
-        print(json.dumps({"i8qk": bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], args.steps, args.warmup, stream)}),
+        print(json.dumps({"i8qk": bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], args.steps, args.warmup, stream,
+                                             power_seconds=args.power_seconds)}),
               flush=True)
         return
     if args.rollout_only:
@@ -619,7 +635,7 @@ def main():
                                              split=split)
         print("[bench] rollout done", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-        res["i8qk"] = bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], 20, 3, stream)
+        res["i8qk"] = bench_i8qk(torch, wf, CONFIGS["i8qk_14b"], 20, 3, stream, power_seconds=args.power_seconds)
         print("[bench] int8-QK done", file=sys.stderr, flush=True)
         res["w8a8"] = bench_w8a8(torch, wf, cfg.nq, 20, 3, stream)
         print("[bench] W8A8 linears done", file=sys.stderr, flush=True)

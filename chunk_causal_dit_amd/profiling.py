@@ -104,9 +104,22 @@ def sample_power(run: Callable[[], None], sync: Callable[[], None], seconds: flo
     if not paths:
         return None
     path = paths[0]
+    # shader clock: hwmon freq1_input (Hz) where the driver has it, else the current
+    # level of pp_dpm_sclk (the line marked "*", in MHz) of the same device
     clk_path = os.path.join(os.path.dirname(path), "freq1_input")
     if not os.path.exists(clk_path):
-        clk_path = None
+        clk_path = os.path.join(os.path.dirname(os.path.dirname(os.path.dirname(path))), "pp_dpm_sclk")
+        if not os.path.exists(clk_path):
+            clk_path = None
+
+    def read_clock_mhz() -> Optional[float]:
+        text = open(clk_path).read()
+        if clk_path.endswith("freq1_input"):
+            return float(text) * 1e-6
+        for line in text.splitlines():
+            if line.rstrip().endswith("*"):
+                return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        return None
     samples: List[float] = []
     clocks: List[float] = []
     stop = threading.Event()
@@ -116,7 +129,9 @@ def sample_power(run: Callable[[], None], sync: Callable[[], None], seconds: flo
             try:
                 samples.append(float(open(path).read()) * 1e-6)
                 if clk_path:
-                    clocks.append(float(open(clk_path).read()) * 1e-6)
+                    c = read_clock_mhz()
+                    if c is not None:
+                        clocks.append(c)
             except (OSError, ValueError):
                 pass
             time.sleep(period)
@@ -135,8 +150,13 @@ def sample_power(run: Callable[[], None], sync: Callable[[], None], seconds: flo
     if not kept:
         return None
     ck = clocks[len(clocks) // 4:]
-    return {"watts": sum(kept) / len(kept), "clock_mhz": (sum(ck) / len(ck)) if ck else None, "calls": calls,
-            "seconds": wall, "sensor": path, "clock_sensor": clk_path}
+    cap_path = os.path.join(os.path.dirname(path), "power1_cap")
+    try:
+        cap = float(open(cap_path).read()) * 1e-6
+    except (OSError, ValueError):
+        cap = None
+    return {"watts": sum(kept) / len(kept), "cap_watts": cap, "clock_mhz": (sum(ck) / len(ck)) if ck else None,
+            "calls": calls, "seconds": wall, "sensor": path, "clock_sensor": clk_path}
 
 
 def main(argv=None):
