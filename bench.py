@@ -624,11 +624,13 @@ def main():
         res["power"] = bench_power(torch, wf, cfg, args.power_seconds, split=split)
         clk = res["power"].get("clock_mhz")
         if clk:
-            # the shader clock the board ran this call at (hwmon, sampled during the power loop),
-            # and the dense bf16 peak at that clock: CUs x 4096 flop/clk x clock
+            # the clock level the driver reported while the call ran back to back (sampled
+            # during the power loop; the counters' GRBM_GUI_ACTIVE / duration gives the lower
+            # effective clock, see profiles/), and the dense bf16 peak at that level:
+            # CUs x 4096 flop/clk x clock
             clk_peak = n_cu * 4096 * clk * 1e6 / 1e12
-            res["roofline"].update({"clock_mhz": clk, "clock_peak_tflops": clk_peak,
-                                    "frac_of_clock_peak": achieved / clk_peak})
+            res["roofline"].update({"dpm_clock_mhz": clk, "dpm_clock_peak_tflops": clk_peak,
+                                    "frac_of_dpm_clock_peak": achieved / clk_peak})
     if not args.no_extras:
         res["rollout"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream, split=split)
         res["rollout_fused"] = bench_rollout(torch, wf, CONFIGS["long_rollout"], 20, 5, stream, fused=True,

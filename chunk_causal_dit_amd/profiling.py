@@ -5,6 +5,8 @@
         --write <write counter_collection.csv> --kernel <name substring> [--kernel <another> ...]
         --copy-bytes <bytes>
         --cmd "<command>" --source <kernel .hip file> --out <file.json>
+    python -m chunk_causal_dit_amd.profiling counters <pmc run dir> [<another pass> ...]
+        --kernel <name substring> --cmd "<command>" --title "<title>" --out <file.md>
 
 ``stats`` turns a ``--kernel-trace --stats`` run into a short markdown table
 (calls, average / min / max duration per kernel). ``traffic`` turns two
@@ -159,6 +161,53 @@ def sample_power(run: Callable[[], None], sync: Callable[[], None], seconds: flo
             "calls": calls, "seconds": wall, "sensor": path, "clock_sensor": clk_path}
 
 
+def counters_markdown(runs: List[str], kernel: str, cmd: str, n_simd: int = 1024, skip_first: bool = True) -> str:
+    """Per-launch counters of one kernel from one or more --pmc runs (directories holding a
+    run_counter_collection.csv and run_kernel_trace.csv; each run one pass of counters).
+    Values are summed over a dispatch's counter instances, then averaged over the kernel's
+    dispatches (the first, a warm-up, dropped when there are more). Derived: the shader
+    clock GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy and MFMA/VALU co-execution as
+    shares of SIMD-cycles (n_simd SIMDs x clock cycles); instructions per wave."""
+    merged: Dict[str, float] = {}
+    clocks, durs = [], []
+    for d in runs:
+        per: Dict[int, Dict[str, float]] = collections.defaultdict(lambda: collections.defaultdict(float))
+        for r in _rows(glob.glob(os.path.join(d, "*counter_collection.csv"))[0]):
+            if kernel in r["Kernel_Name"]:
+                per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        trace = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                 for r in _rows(glob.glob(os.path.join(d, "*kernel_trace.csv"))[0])}
+        ids = sorted(per)
+        if skip_first and len(ids) > 1:
+            ids = ids[1:]
+        for name in per[ids[0]]:
+            merged[name] = sum(per[i][name] for i in ids) / len(ids)
+        if "GRBM_GUI_ACTIVE" in per[ids[0]]:
+            for i in ids:
+                clocks.append(per[i]["GRBM_GUI_ACTIVE"] / 8 / trace[i])
+                durs.append(trace[i])
+    out = [f"Kernel: `{kernel}`", "", f"Command (one run per pass of counters): `{cmd}`", "",
+           "| quantity (per launch, mean over the launches after the first) | value |", "|---|---|"]
+    if durs:
+        out.append(f"| duration under the profiler | {sum(durs) / len(durs) / 1e3:.1f} us |")
+        out.append(f"| shader clock = GRBM_GUI_ACTIVE / 8 / duration | {sum(clocks) / len(clocks):.2f} GHz |")
+    cyc = merged.get("GRBM_GUI_ACTIVE", 0.0) / 8
+    if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in merged:
+        out.append(f"| MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({n_simd} SIMDs x cycles) | "
+                   f"{merged['SQ_VALU_MFMA_BUSY_CYCLES'] / n_simd / cyc * 100:.1f} % |")
+    if cyc and "SQ_VALU_MFMA_COEXEC_CYCLES" in merged:
+        out.append(f"| VALU co-executing with MFMA = SQ_VALU_MFMA_COEXEC_CYCLES / SIMD-cycles | "
+                   f"{merged['SQ_VALU_MFMA_COEXEC_CYCLES'] / n_simd / cyc * 100:.1f} % |")
+    waves = merged.get("SQ_WAVES")
+    for name in sorted(merged):
+        if name in ("GRBM_GUI_ACTIVE",):
+            continue
+        v = merged[name]
+        per_wave = f" ({v / waves:.0f} per wave)" if waves and name.startswith("SQ_INSTS") else ""
+        out.append(f"| {name} | {v:.4g}{per_wave} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -176,7 +225,18 @@ def main(argv=None):
     t.add_argument("--source", required=True)
     t.add_argument("--algorithmic-bytes", type=float, default=None)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("runs", nargs="+", help="rocprofv3 output directories, one per pass of counters")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+    if a.what == "counters":
+        text = f"# {a.title}\n\n" + counters_markdown(a.runs, a.kernel, a.cmd)
+        open(a.out, "w").write(text)
+        print(text)
+        return
     if a.what == "stats":
         text = f"# {a.title}\n\n" + stats_markdown(a.csv, a.cmd)
         open(a.out, "w").write(text)
