@@ -465,6 +465,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     for (int e = 0; e < 8; ++e) pk[kk][e] = (__bf16)0.f;
   float m_ref = -INFINITY;                  // reference max (log2 domain) of this lane's query row
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};     // this half's share of the row sum of weights
+  int gexp = 0;  // I8: every m_ref is a multiple of 2^(gexp - 127) (wave-uniform; 0: no grid yet)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   // per-lane operand offsets inside a stage; every op adds a compile-time constant
   const int k_lane = key_of_arow(qi) * 16 + hh * KSQ * G::KPS;
@@ -540,8 +541,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
   auto vblock = [&](int kt, int cl) {
     float ct = sl2e;   // log2-domain factor of the raw scores
     float bias = 0.f;  // I8: the float bias kMagicF of the integer scores
+    bool regrid = false;
     if constexpr (I8) {
-      ct *= ksc[cl * p.q_blocks + (kt >> 1)];
+      // ct keeps 21 significant bits, so kMagicF * ct = 3 * 2^22 * ct is exact and
+      // a multiple of 2^(E - 22), E its binary exponent. With m_ref on that grid,
+      // the per-row constant -(kMagicF * ct + m_ref) of the weights below is exact
+      // (|m_ref| stays far below kMagicF * ct), so the float bias of the scores
+      // cancels exactly and every tile's weights share one reference.
+      const unsigned cb = __builtin_amdgcn_readfirstlane(__float_as_uint(ct * ksc[cl * p.q_blocks + (kt >> 1)]));
+      ct = __uint_as_float(cb & ~7u);
+      const int gt = (int)((__float_as_uint(kMagicF * ct) >> 23) & 0xffu) - 22;
+      if (gt > gexp) {  // a coarser grid: m_ref moves onto it below
+        gexp = gt;
+        regrid = true;
+      }
       bias = kMagicF;
 #pragma unroll
       for (int b = 0; b < 2; ++b) s[b] = __builtin_bit_cast(f32x16, si[b]);  // kMagicF + score, exactly
@@ -568,7 +581,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
       }
       float mx = halves_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
       const float tmax = (mx - bias) * ct;  // I8: exact subtraction (both in [2^23, 2^24))
-      const float mn = fmaxf(m_ref, tmax);
+      float mn = fmaxf(m_ref, tmax);
+      if (I8 && gexp > 0)  // up to the next multiple of the grid 2^(gexp - 127), exactly
+        mn = ceilf(mn * __uint_as_float((unsigned)(254 - gexp) << 23)) * __uint_as_float((unsigned)gexp << 23);
       const float alpha = fast_exp2(m_ref - mn);
       m_ref = mn;
 #pragma unroll
@@ -580,31 +595,47 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
         for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
     };
     // weights 2^(s ct - m_ref) rounded to bf16, and this lane's share of their sum
-    // (the rounded weights actually used) in four accumulators
+    // in four accumulators: bf16 sums the rounded weights actually used (v_dot2);
+    // I8 sums the fp32 weights with plain adds, which overlap the other wave's
+    // MFMAs where the dot instructions do not.
     auto weights = [&](float (&ts)[4]) {
-      const float nm = I8 ? fmaf(-bias, ct, -m_ref) : -m_ref;  // one rounding of the bias term
+      const float nm = I8 ? fmaf(-bias, ct, -m_ref) : -m_ref;  // I8: exact (see above)
+      if constexpr (I8) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int kk = 0; kk < 4; ++kk) {
+          float w8[8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) pk[2 * b + (e >> 3)][e & 7] = (__bf16)fast_exp2(fmaf(s[b][e], ct, nm));
+          for (int e = 0; e < 8; ++e) {
+            w8[e] = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e], ct, nm));
+            pk[kk][e] = (__bf16)w8[e];
+          }
+          ts[kk] = ((w8[0] + w8[1]) + (w8[2] + w8[3])) + ((w8[4] + w8[5]) + (w8[6] + w8[7]));
+        }
+      } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        ts[kk] = 0.f;
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 pr = {pk[kk][2 * e], pk[kk][2 * e + 1]};
-          ts[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ts[kk], false);
+          for (int e = 0; e < 16; ++e) pk[2 * b + (e >> 3)][e & 7] = (__bf16)fast_exp2(fmaf(s[b][e], ct, nm));
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          ts[kk] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 pr = {pk[kk][2 * e], pk[kk][2 * e + 1]};
+            ts[kk] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ts[kk], false);
+          }
         }
       }
     };
     // Max-free fast path: weights against the current reference max. A lane's
     // 32 weights summing to at most 2^kRescaleLog2 bound every weight by it, as
     // the lazy move above would; a larger, infinite or NaN sum (the first tile,
-    // where m_ref = -inf, or a tile whose max moved up) takes the exact path.
+    // where m_ref = -inf, or a tile whose max moved up) takes the exact path, as
+    // does an I8 tile whose scale needs a coarser grid for m_ref.
     float ts[4];
     weights(ts);
     const float tl = (ts[0] + ts[1]) + (ts[2] + ts[3]);
-    if (__builtin_amdgcn_ballot_w64(!(tl <= kTileSumMax))) {
+    if (regrid || __builtin_amdgcn_ballot_w64(!(tl <= kTileSumMax))) {
       move_max();
       weights(ts);
     }
@@ -635,13 +666,21 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
       wait_vm_barrier<0>();
   };
 
+  // The mid-step barrier only phases the two groups (no LDS stage changes hands
+  // there: the copies of step t write stages that no wave reads in step t). The
+  // bf16 kernel keeps it, which holds the ping-pong and measured less energy per
+  // call; the int8 kernel, whose MFMA block is shorter than its softmax, runs
+  // faster with the waves left to interleave between the step barriers.
+  auto mid_barrier = [&]() {
+    if constexpr (!I8) lds_barrier();
+  };
   if (!wave_on) {  // a wave past the chunk end still copies and meets every barrier
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
-      lds_barrier();
+      mid_barrier();
       copies_and_wait(t, r);
     }
   } else if (grp == 0) {
-    // ping-pong group 0: M_t, barrier, V_t, copies + barrier
+    // ping-pong group 0: M_t, (mid barrier), V_t, copies + barrier
     int vkt = t_base % ktc, vcl = t_base / ktc;
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
       mblock(r);
@@ -649,7 +688,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
         pin_scores(si[0], si[1]);
       else
         pin_scores(s[0], s[1]);
-      lds_barrier();
+      mid_barrier();
       if (t < n_iter) {
         vblock(vkt, vcl);
         if (++vkt == ktc) vkt = 0, ++vcl;
@@ -658,7 +697,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
       copies_and_wait(t, r);
     }
   } else {
-    // ping-pong group 1, half a step behind: V_{t-1}, barrier, M_t, copies + barrier
+    // ping-pong group 1, half a step behind: V_{t-1}, (mid barrier), M_t, copies + barrier
     int vkt = t_base % ktc, vcl = t_base / ktc;
     for (int t = 0, r = 0; t <= n_iter; ++t, r = r == G::NSTAGE - 1 ? 0 : r + 1) {
       if (t >= 1) {
@@ -666,7 +705,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
         if (++vkt == ktc) vkt = 0, ++vcl;
       }
       pin_weights(pk);
-      lds_barrier();
+      mid_barrier();
       mblock(r);
       if constexpr (I8)
         pin_scores(si[0], si[1]);
