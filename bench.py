@@ -17,9 +17,11 @@ attention kernel alone against the bf16 MFMA peak (roofline, timed with
 events on the stream it runs on), chunk-rounds/s, the cache writes against
 HBM bandwidth and, unless --no-extras, the long-rollout round with 3D RoPE,
 the 14B-shaped int8-QK round, the W8A8 linears around attention (QKV and
-O projections of the round's tokens) and whole 1F1C rollouts (4 and 5 steps,
-133 chunks = 399 latent frames: fill, steady state, drain); and the fp64
-oracle timed on the host on a bounded sample of the same round.
+O projections of the round's tokens), library GEMMs in bf16 and int8 at the
+board's power cap (what a plain dense contraction reaches here, beside the
+attention kernels' fractions of the published peaks) and whole 1F1C rollouts
+(4 and 5 steps, 133 chunks = 399 latent frames: fill, steady state, drain);
+and the fp64 oracle timed on the host on a bounded sample of the same round.
 """
 from __future__ import annotations
 
@@ -332,6 +334,59 @@ def bench_i8qk(torch, wf, cfg, steps, warmup, stream, power_seconds=0.0):
     return res
 
 
+def bench_gemm_ceiling(torch, stream, steps, power_seconds):
+    """What a plain dense contraction reaches on this board: library GEMMs (torch.matmul
+    on bf16, torch._int_mm with int32 out), 16384 x 16384 x 8192, timed with HIP events
+    on the launch stream, with the board power and clock while they run back to back.
+    Context for the attention kernels' fractions of the published peaks, which no kernel
+    reaches at the board's power cap."""
+    from chunk_causal_dit_amd.profiling import sample_power
+    M = N = 16384
+    K = 8192
+    res = {"shape_mnk": [M, N, K], "library": "torch.matmul (hipBLASLt) / torch._int_mm"}
+    for name in ("bf16", "i8"):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(15)
+        if name == "bf16":
+            a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16, generator=g)
+            peak = BF16_DENSE_TFLOPS
+
+            def f():
+                return torch.matmul(a, b)
+        else:
+            a = torch.randint(-127, 128, (M, K), device="cuda", dtype=torch.int8, generator=g)
+            b = torch.randint(-127, 128, (N, K), device="cuda", dtype=torch.int8, generator=g).t()
+            peak = INT8_DENSE_TOPS
+
+            def f():
+                return torch._int_mm(a, b)
+        for _ in range(3):
+            f()
+        timers = [Timer(torch, stream, 2) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for t in timers:
+            t.mark(0)
+            f()
+            t.mark(1)
+        torch.cuda.synchronize()
+        ms = np.array([t.ms(0, 1) for t in timers])
+        rate = 2.0 * M * N * K / (np.median(ms) / 1e3) / 1e12
+        leg = {**ms_summary(ms), "t_per_s_median": rate, "frac_of_peak": rate / peak, "peak": peak}
+        if power_seconds > 0:
+            def run():
+                for _ in range(5):
+                    f()
+
+            rec = sample_power(run, torch.cuda.synchronize, power_seconds)
+            if rec is not None:
+                leg.update({"watts": rec["watts"], "cap_watts": rec["cap_watts"], "clock_mhz": rec["clock_mhz"]})
+        res[name] = leg
+        del a, b
+        torch.cuda.empty_cache()
+    return res
+
+
 # Linear shapes of the DiT blocks around attention: (name, out features, in features).
 W8A8_SHAPES = [
     ("wan13b_qkv", 4608, 1536), ("wan13b_o", 1536, 1536),
@@ -508,7 +563,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=4680, help="query rows per chunk in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the rollout, int8-QK, W8A8 and 1F1C rollout measurements")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the rollout, int8-QK, W8A8, library-GEMM and 1F1C rollout measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0, help="run a plain copy of this size first")
     ap.add_argument("--no-split", action="store_true",
                     help="time wf_chunk_causal_attn_fwd (no key split of chunk 0) instead of the workspace call")
@@ -641,6 +697,12 @@ def main():
         print("[bench] int8-QK done", file=sys.stderr, flush=True)
         res["w8a8"] = bench_w8a8(torch, wf, cfg.nq, 20, 3, stream)
         print("[bench] W8A8 linears done", file=sys.stderr, flush=True)
+        ceil = bench_gemm_ceiling(torch, stream, 10, min(args.power_seconds, 2.0))
+        res["gemm_ceiling"] = ceil
+        res["roofline"]["frac_of_library_gemm"] = achieved / ceil["bf16"]["t_per_s_median"]
+        res["i8qk"]["frac_of_library_gemms_mixed"] = res["i8qk"]["effective_tops_median"] / (
+            1.0 / (0.5 / ceil["i8"]["t_per_s_median"] + 0.5 / ceil["bf16"]["t_per_s_median"]))
+        print("[bench] library GEMM ceiling done", file=sys.stderr, flush=True)
         res["rollout_1f1c"] = {
             "4step": bench_rollout_1f1c(torch, wf, 4, 133, 2, cfg.chunk_tokens, cfg.n_heads, cfg.head_dim, stream,
                                         split=split),
