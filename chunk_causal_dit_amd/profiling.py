@@ -161,13 +161,18 @@ def sample_power(run: Callable[[], None], sync: Callable[[], None], seconds: flo
             "calls": calls, "seconds": wall, "sensor": path, "clock_sensor": clk_path}
 
 
-def counters_markdown(runs: List[str], kernel: str, cmd: str, n_simd: int = 1024, skip_first: bool = True) -> str:
+def counters_markdown(runs: List[str], kernel: str, cmd: str, n_simd: int = 1024, skip_first: bool = True,
+                      mfma_per_tile: int = 0) -> str:
     """Per-launch counters of one kernel from one or more --pmc runs (directories holding a
     run_counter_collection.csv and run_kernel_trace.csv; each run one pass of counters).
     Values are summed over a dispatch's counter instances, then averaged over the kernel's
     dispatches (the first, a warm-up, dropped when there are more). Derived: the shader
     clock GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy and MFMA/VALU co-execution as
-    shares of SIMD-cycles (n_simd SIMDs x clock cycles); instructions per wave."""
+    shares of SIMD-cycles (n_simd SIMDs x clock cycles); instructions per wave; and, when
+    the busy, co-execution and SQ_ACTIVE_INST_VALU counters are all present, the split of
+    SIMD time into MFMA only, VALU only, both and neither (SQ_ACTIVE_INST_* count 4-cycle
+    units). With mfma_per_tile > 0 the instruction counts are also given per key tile and
+    wave (MFMA instructions per wave / mfma_per_tile tiles)."""
     merged: Dict[str, float] = {}
     clocks, durs = [], []
     for d in runs:
@@ -205,6 +210,29 @@ def counters_markdown(runs: List[str], kernel: str, cmd: str, n_simd: int = 1024
         v = merged[name]
         per_wave = f" ({v / waves:.0f} per wave)" if waves and name.startswith("SQ_INSTS") else ""
         out.append(f"| {name} | {v:.4g}{per_wave} |")
+    need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU")
+    if cyc and all(n in merged for n in need):
+        simd_cyc = n_simd * cyc
+        mf = merged["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cyc
+        both = merged["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cyc
+        va = merged["SQ_ACTIVE_INST_VALU"] * 4 / simd_cyc
+        out += ["", "| share of SIMD-cycles | value |", "|---|---|",
+                f"| MFMA busy | {mf * 100:.1f} % |", f"| VALU issuing (SQ_ACTIVE_INST_VALU x 4) | {va * 100:.1f} % |",
+                f"| both at once (SQ_VALU_MFMA_COEXEC_CYCLES) | {both * 100:.1f} % |",
+                f"| MFMA only | {(mf - both) * 100:.1f} % |", f"| VALU only | {(va - both) * 100:.1f} % |",
+                f"| neither (barrier waits, LDS and SMEM latency, scalar-only issue) | "
+                f"{(1 - mf - va + both) * 100:.1f} % |"]
+    if mfma_per_tile and waves and "SQ_INSTS_MFMA" in merged:
+        tiles = merged["SQ_INSTS_MFMA"] / waves / mfma_per_tile
+        rows = [("MFMA", "SQ_INSTS_MFMA"), ("LDS instructions", "SQ_INSTS_LDS"),
+                ("VALU instructions (MFMA included)", "SQ_INSTS_VALU"), ("of which v_exp_f32 and other fp32 "
+                                                                        "transcendentals", "SQ_INSTS_VALU_TRANS_F32"),
+                ("SALU instructions", "SQ_INSTS_SALU")]
+        out += ["", f"Per 64-key tile and wave ({tiles:.0f} tiles per wave = MFMA per wave / {mfma_per_tile}):", "",
+                "| instructions | per tile and wave |", "|---|---|"]
+        for label, name in rows:
+            if name in merged:
+                out.append(f"| {label} | {merged[name] / waves / tiles:.1f} |")
     return "\n".join(out) + "\n"
 
 
@@ -216,6 +244,7 @@ def main(argv=None):
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--title", default="rocprofv3 --kernel-trace --stats")
+    s.add_argument("--note", default="", help="text appended after the table")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -231,14 +260,20 @@ def main(argv=None):
     c.add_argument("--cmd", required=True)
     c.add_argument("--title", required=True)
     c.add_argument("--out", required=True)
+    c.add_argument("--mfma-per-tile", type=int, default=0, help="MFMA instructions per key tile and wave")
+    c.add_argument("--note", default="", help="text appended after the tables")
     a = ap.parse_args(argv)
     if a.what == "counters":
-        text = f"# {a.title}\n\n" + counters_markdown(a.runs, a.kernel, a.cmd)
+        text = f"# {a.title}\n\n" + counters_markdown(a.runs, a.kernel, a.cmd, mfma_per_tile=a.mfma_per_tile)
+        if a.note:
+            text += "\n" + a.note.strip() + "\n"
         open(a.out, "w").write(text)
         print(text)
         return
     if a.what == "stats":
         text = f"# {a.title}\n\n" + stats_markdown(a.csv, a.cmd)
+        if a.note:
+            text += "\n" + a.note.strip() + "\n"
         open(a.out, "w").write(text)
         print(text)
         return
