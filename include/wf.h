@@ -245,8 +245,10 @@ int wf_chunk_causal_attn_fwd_static(const void* q, const wf_kv_cache* kv, int n_
  *   Q and K - mean are quantized per head in blocks of 128 tokens that start
  *   at every chunk start: s = amax/127 (1 if amax = 0), code =
  *   clamp(round_half_even(x/s), -127, 127), all decisions in fp32;
- *   S = int32 dot products of the codes times s_q * s_k * scale; softmax
- *   fp32; P rounded to bf16; P.V in bf16 with fp32 accumulation.
+ *   S = int32 dot products of the codes times s_q * s_k * scale (the
+ *   kernel's log2-domain factor s_q * s_k * scale * log2(e) keeps 21
+ *   significant bits); softmax fp32; P rounded to bf16; P.V in bf16 with
+ *   fp32 accumulation; the softmax denominator sums the fp32 weights.
  * The mean shift changes no softmax row; lse refers to the unshifted keys
  * (the kernel adds scale * <q^_i, mean_h>, q^ the dequantized query).
  * workspace: device memory of wf_attn_i8qk_workspace_bytes() bytes, 256-byte
