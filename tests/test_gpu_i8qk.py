@@ -153,6 +153,42 @@ def test_i8_14b_round_all_rows():
     check_outputs(inp, out, lse, ref)
 
 
+def test_i8_block_scales_spread():
+    """K blocks scaled by factors from 1/1000 to 60 (Q blocks by 1/8 to 2), so the
+    log2-domain factors of a row's tiles span about 2^11: the power-of-two grid the
+    kernel keeps its reference max on coarsens several times inside a row, and the
+    exact-max path runs often. Quantization bit-exact; O and LSE against the
+    quantized oracle at the bf16 bounds (no comparison with unquantized attention:
+    a key mean dominated by the large blocks leaves the small ones few levels)."""
+    wf = RL.require_gpu()
+    cfg = RoundConfig("i8_spread", 2, 128, 300, 3, 3, "bf16", seed=60, int8_qk=True)
+    print(f"[case] {cfg.name}", flush=True)
+    inp = make_round_inputs(cfg)
+    C, nb = cfg.chunk_tokens, -(-cfg.chunk_tokens // 128)
+    kf = [1.0, 1e-3, 20.0, 1.0 / 16, 60.0, 0.5, 7.0]
+    qf = [1.0, 0.125, 2.0]
+
+    def scale_blocks(x, factors, n_chunks, salt):
+        for c in range(n_chunks):
+            for b in range(nb):
+                rows = slice(c * C + b * 128, min(c * C + (b + 1) * 128, (c + 1) * C))
+                x[rows] = round_to_bf16(x[rows] * np.float32(factors[(c * nb + b + salt) % len(factors)]))
+
+    scale_blocks(inp.k_hist, kf, cfg.n_hist, 0)
+    scale_blocks(inp.k_in, kf, cfg.n_inflight, 3)
+    scale_blocks(inp.q, qf, cfg.n_inflight, 0)
+    out, lse, cache, ws = run_i8(wf, inp)
+    ref = check_quantization(inp, cache, ws)
+    k_vis, v_vis = visible_keys(inp)
+    o_q, l_q = OQ.quantized_attention(inp.q, k_vis, v_vis, cfg.n_hist, C, cfg.scale,
+                                      workers=RL.oracle_workers(), quant=ref)
+    RL.assert_close(out.float().cpu().numpy(), o_q, "bf16", f"{cfg.name} O vs quantized oracle")
+    dl = np.abs(lse.cpu().numpy() - l_q).max()
+    print(f"[parity] {cfg.name} LSE vs quantized oracle: max abs {dl:.3e} (|LSE| up to {np.abs(l_q).max():.1f})",
+          flush=True)
+    assert dl <= LSE_ATOL
+
+
 def test_i8_permuted_slots_bitwise():
     wf = RL.require_gpu()
     cfg = RoundConfig("i8_perm", 2, 128, 300, 3, 3, "bf16", seed=56, int8_qk=True)
