@@ -18,8 +18,9 @@ events on the stream it runs on), chunk-rounds/s, the cache writes against
 HBM bandwidth and, unless --no-extras, the long-rollout round with 3D RoPE,
 the 14B-shaped int8-QK round, the W8A8 linears around attention (QKV and
 O projections of the round's tokens), library GEMMs in bf16 and int8 at the
-board's power cap (what a plain dense contraction reaches here, beside the
-attention kernels' fractions of the published peaks) and whole 1F1C rollouts
+board's power cap and a plain device copy (what a dense contraction and a
+streaming kernel reach here, beside the fractions of the published peaks) and
+whole 1F1C rollouts
 (4 and 5 steps, 133 chunks = 399 latent frames: fill, steady state, drain);
 and the fp64 oracle timed on the host on a bounded sample of the same round.
 """
@@ -344,6 +345,25 @@ def bench_gemm_ceiling(torch, stream, steps, power_seconds):
     M = N = 16384
     K = 8192
     res = {"shape_mnk": [M, N, K], "library": "torch.matmul (hipBLASLt) / torch._int_mm"}
+    # a plain device copy (1 GiB of bf16, read once and written once): the HBM rate a
+    # streaming kernel reaches here, beside the published 8 TB/s
+    src = torch.ones(512 * 1024 * 1024, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    timers = [Timer(torch, stream, 2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for t in timers:
+        t.mark(0)
+        dst.copy_(src)
+        t.mark(1)
+    torch.cuda.synchronize()
+    ms = np.array([t.ms(0, 1) for t in timers])
+    moved = 2.0 * src.numel() * src.element_size()
+    res["copy"] = {**ms_summary(ms), "bytes_moved": moved, "gbs_median": moved / (np.median(ms) / 1e3) / 1e9,
+                   "frac_of_hbm_peak": moved / (np.median(ms) / 1e3) / 1e9 / HBM_GBS}
+    del src, dst
+    torch.cuda.empty_cache()
     for name in ("bf16", "i8"):
         g = torch.Generator(device="cuda")
         g.manual_seed(15)
@@ -700,6 +720,7 @@ def main():
         ceil = bench_gemm_ceiling(torch, stream, 10, min(args.power_seconds, 2.0))
         res["gemm_ceiling"] = ceil
         res["roofline"]["frac_of_library_gemm"] = achieved / ceil["bf16"]["t_per_s_median"]
+        res["kv_writes"]["frac_of_plain_copy"] = res["kv_writes"]["gbs_median"] / ceil["copy"]["gbs_median"]
         res["i8qk"]["frac_of_library_gemms_mixed"] = res["i8qk"]["effective_tops_median"] / (
             1.0 / (0.5 / ceil["i8"]["t_per_s_median"] + 0.5 / ceil["bf16"]["t_per_s_median"]))
         print("[bench] library GEMM ceiling done", file=sys.stderr, flush=True)
