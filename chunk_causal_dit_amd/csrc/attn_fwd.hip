@@ -544,10 +544,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(wf::AttnParams p
     bool regrid = false;
     if constexpr (I8) {
       // ct is rounded to 21 significant bits, so kMagicF * ct = 3 * 2^22 * ct is exact and
-      // a multiple of 2^(E - 22), E its binary exponent. With m_ref on that grid,
-      // the per-row constant -(kMagicF * ct + m_ref) of the weights below is exact
-      // (|m_ref| stays far below kMagicF * ct), so the float bias of the scores
-      // cancels exactly and every tile's weights share one reference.
+      // a multiple of 2^(E - 22), E its binary exponent. With m_ref on that grid and
+      // |m_ref| <= 2^(E + 1) (scores are below 2^22, so a row's max in log2 units is far
+      // below kMagicF * ct unless another tile's factor is much larger), the per-row
+      // constant -(kMagicF * ct + m_ref) of the weights below is exact: the float bias
+      // of the scores cancels exactly and every tile's weights share one reference.
+      // Otherwise the constant rounds at the fp32 precision of m_ref itself.
       const unsigned cb = __builtin_amdgcn_readfirstlane(__float_as_uint(ct * ksc[cl * p.q_blocks + (kt >> 1)]));
       ct = __uint_as_float((cb + 4u) & ~7u);  // nearest (ties up); a carry gives a power of two
       const int gt = (int)((__float_as_uint(kMagicF * ct) >> 23) & 0xffu) - 22;
