@@ -75,6 +75,31 @@ def build(verbose: bool = False, jobs: int = 4, out: str = LIB) -> str:
     return out
 
 
+C_CONSUMER_SRC = os.path.join(ROOT, "tests", "c_consumer", "wf_round.c")
+C_CONSUMER = os.path.join(ROOT, "tests", "c_consumer", "wf_round")
+
+
+def build_c_consumer(verbose: bool = False) -> str:
+    """Compile the plain-C consumer of the ABI (tests/c_consumer/wf_round.c) with gcc as
+    C11 against include/wf.h, linked to libwf.so next to this file and to the HIP runtime.
+    Returns the program's path."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for the C consumer")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    rpath = os.path.relpath(HERE, os.path.dirname(C_CONSUMER))
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-isystem", f"{rocm}/include", f"-I{INCLUDE}", C_CONSUMER_SRC, "-o", C_CONSUMER,
+           f"-L{HERE}", "-l:libwf.so", f"-L{rocm}/lib", "-lamdhip64",
+           f"-Wl,-rpath,$ORIGIN/{rpath}", f"-Wl,-rpath,{rocm}/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if res.returncode != 0:
+        raise RuntimeError("C consumer build failed:\n" + res.stdout.decode(errors="replace"))
+    return C_CONSUMER
+
+
 def _drain(procs):
     while procs:
         src, p = procs.pop(0)
@@ -90,3 +115,4 @@ def _drain(procs):
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_consumer(verbose="-v" in sys.argv))
