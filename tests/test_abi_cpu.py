@@ -243,6 +243,30 @@ def test_workspace_overlap_refused(L):
     L.wf_kv_cache_destroy(h)
 
 
+def test_i8qk_scale_table_limit(L):
+    """The int8 call keeps the K block scales of every table entry in LDS: table length x
+    128-token blocks per chunk must stay <= 16384. 64 entries of 257 blocks (C = 32,896)
+    are refused on the host with WF_E_SHAPE; 64 x 256 blocks pass that check (and, with
+    no GPU, fail only at the launch)."""
+    h, pools = make_cache(L, n_slots=64, C=128 * 257, H=1, D=128)
+    assert set_table(L, h, list(range(64))) == WF_OK
+    q = ctypes.c_void_p(pools.k.value)
+    ws = ctypes.c_void_p(pools.v.value + (1 << 20))
+    g = L.wf_chunk_causal_attn_fwd_i8qk
+    assert g(q, h, 2, 0.1, ws, q, None, None) == WF_E_SHAPE
+    assert b"exceeds 16384" in L.wf_last_error()
+    L.wf_kv_cache_destroy(h)
+    import torch
+
+    if not torch.cuda.is_available():  # the pointers are host stand-ins: launch only where it fails cleanly
+        h, pools = make_cache(L, n_slots=64, C=128 * 256, H=1, D=128)
+        assert set_table(L, h, list(range(64))) == WF_OK
+        q = ctypes.c_void_p(pools.k.value)
+        assert g(q, h, 2, 0.1, ws, q, None, None) == WF_E_HIP
+        assert b"exceeds 16384" not in L.wf_last_error()
+        L.wf_kv_cache_destroy(h)
+
+
 def test_attention_launch_size_limit(L):
     """A round whose launch would exceed 2^32 work-items is refused on the host:
     2^20-token chunks x 1024 heads (the largest shape a cache accepts)."""
