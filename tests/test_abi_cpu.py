@@ -261,8 +261,8 @@ def test_i8qk_scale_table_limit(L):
     if not torch.cuda.is_available():  # the pointers are host stand-ins: launch only where it fails cleanly
         h, pools = make_cache(L, n_slots=64, C=128 * 256, H=1, D=128)
         assert set_table(L, h, list(range(64))) == WF_OK
-        q = ctypes.c_void_p(pools.k.value)
-        assert g(q, h, 2, 0.1, ws, q, None, None) == WF_E_HIP
+        far = lambda gib: ctypes.c_void_p(pools.k.value + (gib << 30))  # past the 0.5 GiB pools, disjoint
+        assert g(far(4), h, 2, 0.1, far(6), far(5), None, None) == WF_E_HIP, L.wf_last_error()
         assert b"exceeds 16384" not in L.wf_last_error()
         L.wf_kv_cache_destroy(h)
 
